@@ -1,0 +1,644 @@
+// swiglu_mlp.hip -- fused SwiGLU MLP kernels for gfx950 and the C ABI of
+// include/swiglu_mlp.h.
+//
+// The method is the one of "[RFC] Full-pipeline SwiGLU MLP with
+// forward/backward co-optimization" (Liger-Kernel issue #1347), section
+// "Summary". Its steps map onto launches of one MFMA tile engine
+// (gemm_tile.hpp), each with its own operand layouts and epilogue:
+//
+//  stage  computes                                  M x N x K    A op / B op
+//  0      G = X Wg, U = X Wu, A = SiLU(G) U         T x H x D    KC / MC (two B sources)
+//  1      Y = A Wd                                  T x D x H    KC / MC
+//  2      dA = dY Wd^T -> dG, dU over G, U          T x H x D    KC / KC
+//  3      dWd = A^T dY                              H x D x T    MC / MC
+//  4      [dWg | dWu] = X^T [dG | dU]               D x H x T    MC / MC (grid z = 2)
+//  5      dI = dG Wg^T + dU Wu^T                    T x D x 2H   KC / KC (two K halves)
+//  6,7    no-grad: stage 0 writing only A, then stage 1
+//
+// Numerics: fp32 accumulation; each stored value is rounded once to the
+// storage type. The forward epilogue is the one-round program of "Scope
+// one-round FP32 SwiGLU to the exact Qwen3.5 contract" (xorl PR #51, review
+// thread), applied to the stored (already rounded) g and u so that the saved
+// A, G and U are mutually consistent; the backward epilogue likewise works in
+// fp32 from the fp32 dA accumulator and the stored g and u, rounding dG and
+// dU once.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gemm_tile.hpp"
+#include "../../include/swiglu_mlp.h"
+
+namespace swiglu {
+
+enum Kind { GATEUP = 0, PLAIN = 1, DSWIGLU = 2, DX = 3 };
+
+struct KArgs {
+  Operand a0, a1;  // A operand; a1 = second K half (DX)
+  Operand b0, b1;  // B operand; b1 = second N half (GATEUP), second K half (DX), z = 1 (PLAIN)
+  char* c0;        // PLAIN/DX: C; GATEUP: A plane; DSWIGLU: G plane (in/out)
+  char* c1;        // PLAIN: C for z = 1; GATEUP: G plane; DSWIGLU: U plane (in/out)
+  char* c2;        // GATEUP: U plane
+  int64_t ldc;     // elements
+  int M, N;        // output extent (GATEUP: N = H)
+  int tiles_m, tiles_n;
+  int store_gu;    // GATEUP: write the G and U planes (training) or A only (no-grad)
+};
+
+// SiLU and its derivative in fp32 from a stored gate value.
+__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+template <class E, int BM, int BN, int AL, int BL, int KIND>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mlp_gemm(const KArgs g) {
+  using Geo = Geometry<E, BM, BN, AL, BL>;
+  constexpr int EB = E::kBytes;
+  constexpr int BK = E::kBK;
+  constexpr int TM = Geo::TM, TN = Geo::TN;
+  __shared__ __attribute__((aligned(16))) char smem[Geo::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(g.tiles_m, g.tiles_n, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = (KIND == GATEUP) ? tn * (BN / 2) : tn * BN;
+
+  Operand A = g.a0, B = g.b0;
+  char* C = g.c0;
+  if (KIND == PLAIN && blockIdx.z == 1) {
+    B = g.b1;
+    C = g.c1;
+  }
+
+  int a_rows[TM], b_rows[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_rows[i] = wm * Geo::WTM + i * 32;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    if constexpr (KIND == GATEUP) {
+      // G columns in LDS rows [0, BN/2), U columns in [BN/2, BN); wave wn
+      // owns the same BN/4 hidden units of both.
+      constexpr int H2 = TN / 2;
+      b_rows[j] = (j < H2 ? 0 : BN / 2) + wn * (BN / 4) + (j % H2) * 32;
+    } else {
+      b_rows[j] = wn * Geo::WTN + j * 32;
+    }
+  }
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
+
+  TileLoader<E, BM, AL> la;
+  // GATEUP fills the B tile from two sources of BN/2 rows each.
+  constexpr int RB = (KIND == GATEUP) ? BN / 2 : BN;
+  TileLoader<E, RB, BL, BN> lb0;
+  TileLoader<E, RB, BL, BN> lb1;
+
+  const int nk1 = (A.k + BK - 1) / BK;
+  const int nk = (KIND == DX) ? 2 * nk1 : nk1;
+
+  auto load = [&](int kt) {
+    if constexpr (KIND == DX) {
+      bool second = kt >= nk1;
+      int k0 = (second ? kt - nk1 : kt) * BK;
+      la.load(second ? g.a1 : g.a0, m0, k0, tid);
+      lb0.load(second ? g.b1 : g.b0, n0, k0, tid);
+    } else {
+      int k0 = kt * BK;
+      la.load(A, m0, k0, tid);
+      lb0.load(B, n0, k0, tid);
+      if constexpr (KIND == GATEUP) lb1.load(g.b1, n0, k0, tid);
+    }
+  };
+  auto store = [&](int stage) {
+    char* sa = smem + stage * Geo::STAGE;
+    char* sb = sa + Geo::A_BYTES;
+    la.store(sa, tid);
+    lb0.store(sb, tid, 0);
+    if constexpr (KIND == GATEUP) lb1.store(sb, tid, BN / 2);
+  };
+
+  if (nk > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+    const char* sa = smem + cur * Geo::STAGE;
+    mma_stage<E, BM, BN, AL, BL, TM, TN>(sa, sa + Geo::A_BYTES, a_rows, b_rows, acc, lane);
+    if (kt + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----------------------------------------------------------
+  // acc[i][j][r]: m = m0 + a_rows[i] + (lane & 31),
+  //               n = (column base of subtile j) + (r / 4) * 8 + (lane / 32) * 4 + r % 4.
+  using V4 = typename E::vec4;
+  const int ml = lane & 31;
+  const int nl = (lane >> 5) * 4;
+  if constexpr (KIND == GATEUP) {
+    constexpr int H2 = TN / 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + a_rows[i] + ml;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < H2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * (BN / 4) + j * 32 + q * 8 + nl;
+          if (n >= g.N) continue;
+          V4 gv, uv, av;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            typename E::elem gs = E::from_f32(acc[i][j][q * 4 + e]);
+            typename E::elem us = E::from_f32(acc[i][j + H2][q * 4 + e]);
+            float gf = E::to_f32(gs), uf = E::to_f32(us);
+            gv[e] = gs;
+            uv[e] = us;
+            av[e] = E::from_f32(gf * sigmoid_f32(gf) * uf);
+          }
+          const int64_t off = ((int64_t)m * g.ldc + n) * EB;
+          *(V4*)(g.c0 + off) = av;
+          if (g.store_gu) {
+            *(V4*)(g.c1 + off) = gv;
+            *(V4*)(g.c2 + off) = uv;
+          }
+        }
+      }
+    }
+  } else if constexpr (KIND == DSWIGLU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + a_rows[i] + ml;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + b_rows[j] + q * 8 + nl;
+          if (n >= g.N) continue;
+          const int64_t off = ((int64_t)m * g.ldc + n) * EB;
+          V4 gv = *(const V4*)(g.c0 + off);
+          V4 uv = *(const V4*)(g.c1 + off);
+          V4 dg, du;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float da = acc[i][j][q * 4 + e];
+            float gf = E::to_f32(gv[e]), uf = E::to_f32(uv[e]);
+            float s = sigmoid_f32(gf);
+            du[e] = E::from_f32(da * (gf * s));
+            dg[e] = E::from_f32(da * uf * (s * (1.0f + gf * (1.0f - s))));
+          }
+          *(V4*)(g.c0 + off) = dg;
+          *(V4*)(g.c1 + off) = du;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + a_rows[i] + ml;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + b_rows[j] + q * 8 + nl;
+          if (n >= g.N) continue;
+          V4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = E::from_f32(acc[i][j][q * 4 + e]);
+          *(V4*)(C + ((int64_t)m * g.ldc + n) * EB) = v;
+        }
+      }
+    }
+  }
+}
+
+// Fill kernel (used to clear weight gradients when T = 0 would otherwise
+// leave them unwritten; a kernel rather than a memset so that callers may
+// capture the path in a graph).
+__global__ void fill_zero(u32x4_t* p, int64_t n16) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i < n16; i += (int64_t)gridDim.x * blockDim.x) p[i] = u32x4_t{0, 0, 0, 0};
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+// Stage timing (profiling aid).
+struct Timer {
+  bool on = false;
+  int cap = 0;
+  int count[SWIGLU_NUM_STAGES] = {};
+  hipEvent_t* ev[SWIGLU_NUM_STAGES] = {};  // 2 * cap events per stage
+};
+static Timer g_timer;
+
+struct StageScope {
+  int s;
+  hipStream_t st;
+  bool rec = false;
+  StageScope(int stage, hipStream_t stream) : s(stage), st(stream) {
+    if (g_timer.on && g_timer.count[s] < g_timer.cap) {
+      rec = true;
+      (void)hipEventRecord(g_timer.ev[s][2 * g_timer.count[s]], st);
+    }
+  }
+  ~StageScope() {
+    if (rec) {
+      (void)hipEventRecord(g_timer.ev[s][2 * g_timer.count[s] + 1], st);
+      g_timer.count[s]++;
+    }
+  }
+};
+
+static inline Operand opnd(const void* p, int64_t ld, int64_t rows, int64_t k) {
+  return Operand{(const char*)p, ld, (int)rows, (int)k};
+}
+
+template <class E, int BM, int BN, int AL, int BL, int KIND>
+static int launch(KArgs a, int grid_z, int stage, hipStream_t stream) {
+  const int nb = a.tiles_m * a.tiles_n;
+  if (nb <= 0) return SWIGLU_OK;
+  StageScope scope(stage, stream);
+  hipLaunchKernelGGL((mlp_gemm<E, BM, BN, AL, BL, KIND>), dim3(nb, 1, grid_z), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Rows of X per workgroup tile for the T-indexed GEMMs. Small token counts
+// (the no-grad shapes) use short tiles so that more workgroups share the
+// weight stream.
+static inline bool small_t(int64_t T) { return T <= 512; }
+
+template <class E>
+struct Path {
+  static constexpr int EB = E::kBytes;
+
+  static int gateup(const void* X, const void* Wg, const void* Wu, char* Ap, char* Gp, char* Up,
+                    int64_t T, int64_t D, int64_t H, bool store_gu, int stage, hipStream_t s) {
+    KArgs a{};
+    a.a0 = opnd(X, D, T, D);
+    a.b0 = opnd(Wg, H, H, D);
+    a.b1 = opnd(Wu, H, H, D);
+    a.c0 = Ap;
+    a.c1 = Gp;
+    a.c2 = Up;
+    a.ldc = H;
+    a.M = (int)T;
+    a.N = (int)H;
+    a.store_gu = store_gu ? 1 : 0;
+    if (small_t(T)) {
+      a.tiles_m = cdiv(T, 64);
+      a.tiles_n = cdiv(H, 128);
+      return launch<E, 64, 256, KC, MC, GATEUP>(a, 1, stage, s);
+    }
+    a.tiles_m = cdiv(T, 256);
+    a.tiles_n = cdiv(H, 128);
+    return launch<E, 256, 256, KC, MC, GATEUP>(a, 1, stage, s);
+  }
+
+  static int down(const char* Ap, const void* Wd, void* Y, int64_t T, int64_t D, int64_t H, int stage,
+                  hipStream_t s) {
+    KArgs a{};
+    a.a0 = opnd(Ap, H, T, H);
+    a.b0 = opnd(Wd, D, D, H);
+    a.c0 = (char*)Y;
+    a.ldc = D;
+    a.M = (int)T;
+    a.N = (int)D;
+    if (small_t(T)) {
+      a.tiles_m = cdiv(T, 64);
+      a.tiles_n = cdiv(D, 256);
+      return launch<E, 64, 256, KC, MC, PLAIN>(a, 1, stage, s);
+    }
+    a.tiles_m = cdiv(T, 256);
+    a.tiles_n = cdiv(D, 256);
+    return launch<E, 256, 256, KC, MC, PLAIN>(a, 1, stage, s);
+  }
+
+  static int dgu(const void* dY, const void* Wd, char* Gp, char* Up, int64_t T, int64_t D, int64_t H,
+                 hipStream_t s) {
+    KArgs a{};
+    a.a0 = opnd(dY, D, T, D);
+    a.b0 = opnd(Wd, D, H, D);  // Bop[k=d][n=h] = Wd[h][d]: K-contiguous rows of Wd
+    a.c0 = Gp;
+    a.c1 = Up;
+    a.ldc = H;
+    a.M = (int)T;
+    a.N = (int)H;
+    if (small_t(T)) {
+      a.tiles_m = cdiv(T, 64);
+      a.tiles_n = cdiv(H, 256);
+      return launch<E, 64, 256, KC, KC, DSWIGLU>(a, 1, 2, s);
+    }
+    a.tiles_m = cdiv(T, 256);
+    a.tiles_n = cdiv(H, 256);
+    return launch<E, 256, 256, KC, KC, DSWIGLU>(a, 1, 2, s);
+  }
+
+  static int dwd(const char* Ap, const void* dY, void* dWd, int64_t T, int64_t D, int64_t H, hipStream_t s) {
+    KArgs a{};
+    a.a0 = opnd(Ap, H, H, T);  // Aop[m=h][k=t] = A[t][h]
+    a.b0 = opnd(dY, D, D, T);  // Bop[k=t][n=d] = dY[t][d]
+    a.c0 = (char*)dWd;
+    a.ldc = D;
+    a.M = (int)H;
+    a.N = (int)D;
+    a.tiles_m = cdiv(H, 256);
+    a.tiles_n = cdiv(D, 256);
+    return launch<E, 256, 256, MC, MC, PLAIN>(a, 1, 3, s);
+  }
+
+  static int dwgu(const void* X, const char* dGp, const char* dUp, void* dWg, void* dWu, int64_t T, int64_t D,
+                  int64_t H, hipStream_t s) {
+    KArgs a{};
+    a.a0 = opnd(X, D, D, T);    // Aop[m=d][k=t] = X[t][d]
+    a.b0 = opnd(dGp, H, H, T);  // Bop[k=t][n=h] = dG[t][h]
+    a.b1 = opnd(dUp, H, H, T);
+    a.c0 = (char*)dWg;
+    a.c1 = (char*)dWu;
+    a.ldc = H;
+    a.M = (int)D;
+    a.N = (int)H;
+    a.tiles_m = cdiv(D, 256);
+    a.tiles_n = cdiv(H, 256);
+    return launch<E, 256, 256, MC, MC, PLAIN>(a, 2, 4, s);
+  }
+
+  static int dx(const char* dGp, const char* dUp, const void* Wg, const void* Wu, void* dX, int64_t T, int64_t D,
+                int64_t H, hipStream_t s) {
+    KArgs a{};
+    a.a0 = opnd(dGp, H, T, H);
+    a.a1 = opnd(dUp, H, T, H);
+    a.b0 = opnd(Wg, H, D, H);  // Bop[k=h][n=d] = Wg[d][h]: K-contiguous rows of Wg
+    a.b1 = opnd(Wu, H, D, H);
+    a.c0 = (char*)dX;
+    a.ldc = D;
+    a.M = (int)T;
+    a.N = (int)D;
+    if (small_t(T)) {
+      a.tiles_m = cdiv(T, 64);
+      a.tiles_n = cdiv(D, 256);
+      return launch<E, 64, 256, KC, KC, DX>(a, 1, 5, s);
+    }
+    a.tiles_m = cdiv(T, 256);
+    a.tiles_n = cdiv(D, 256);
+    return launch<E, 256, 256, KC, KC, DX>(a, 1, 5, s);
+  }
+};
+
+// ---- validation ----------------------------------------------------------
+
+static size_t elt_bytes(int dt) { return dt == SWIGLU_FP32 ? 4 : (dt == SWIGLU_BF16 || dt == SWIGLU_FP16 ? 2 : 0); }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+static bool overlap(Range a, Range b) {
+  if (a.n == 0 || b.n == 0) return false;
+  uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Pointers to non-empty buffers must be non-NULL and 16-byte aligned;
+// a buffer of zero bytes (T = 0) may be NULL.
+static int check_ptrs(const Range* r, int n) {
+  for (int i = 0; i < n; ++i)
+    if (r[i].n > 0 && !r[i].p) return SWIGLU_ERR_NULL;
+  for (int i = 0; i < n; ++i)
+    if (r[i].p && !aligned16(r[i].p)) return SWIGLU_ERR_ALIGN;
+  return SWIGLU_OK;
+}
+
+static int check_shape(int64_t T, int64_t D, int64_t H) {
+  if (T < 0 || D <= 0 || H <= 0) return SWIGLU_ERR_SHAPE;
+  if ((D & 7) || (H & 7)) return SWIGLU_ERR_SHAPE;
+  // int32 element counts inside the kernels: rows and K extents, and byte
+  // offsets of one tile row stay below 2^31.
+  if (T > 0x7fffffffLL || D > (1 << 24) || H > (1 << 24)) return SWIGLU_ERR_SHAPE;
+  return SWIGLU_OK;
+}
+
+static int check_device() {
+  static int cached[64];  // 0 unknown, 1 ok, 2 bad
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SWIGLU_ERR_DEVICE;
+  if (cached[dev] == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return SWIGLU_ERR_DEVICE;
+    cached[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return cached[dev] == 1 ? SWIGLU_OK : SWIGLU_ERR_DEVICE;
+}
+
+static int zero_fill(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return SWIGLU_OK;
+  int64_t n16 = (int64_t)(bytes / 16);
+  int blocks = (int)((n16 + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero, dim3(blocks), dim3(256), 0, s, (u32x4_t*)p, n16);
+  return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+template <class E>
+static int run_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
+                   int64_t D, int64_t H, hipStream_t s) {
+  const size_t plane = (size_t)T * H * E::kBytes;
+  char* Ap = (char*)saved;
+  int rc = Path<E>::gateup(X, Wg, Wu, Ap, Ap + plane, Ap + 2 * plane, T, D, H, true, 0, s);
+  if (rc) return rc;
+  return Path<E>::down(Ap, Wd, Y, T, D, H, 1, s);
+}
+
+template <class E>
+static int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
+                   void* dX, void* dWg, void* dWu, void* dWd, int64_t T, int64_t D, int64_t H, hipStream_t s) {
+  const size_t plane = (size_t)T * H * E::kBytes;
+  char* Ap = (char*)saved;
+  char* Gp = Ap + plane;
+  char* Up = Ap + 2 * plane;
+  int rc = Path<E>::dgu(dY, Wd, Gp, Up, T, D, H, s);
+  if (rc) return rc;
+  if ((rc = Path<E>::dwd(Ap, dY, dWd, T, D, H, s))) return rc;
+  if ((rc = Path<E>::dwgu(X, Gp, Up, dWg, dWu, T, D, H, s))) return rc;
+  return Path<E>::dx(Gp, Up, Wg, Wu, dX, T, D, H, s);
+}
+
+template <class E>
+static int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws, int64_t T,
+                     int64_t D, int64_t H, hipStream_t s) {
+  char* Ap = (char*)ws;
+  int rc = Path<E>::gateup(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, 6, s);
+  if (rc) return rc;
+  return Path<E>::down(Ap, Wd, Y, T, D, H, 7, s);
+}
+
+}  // namespace swiglu
+
+using namespace swiglu;
+
+extern "C" {
+
+size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype) {
+  size_t e = elt_bytes(dtype);
+  if (!e || T < 0 || H <= 0) return 0;
+  return 3 * (size_t)T * (size_t)H * e;
+}
+
+size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype) {
+  size_t e = elt_bytes(dtype);
+  if (!e || T < 0 || D <= 0 || H <= 0) return 0;
+  return (size_t)T * (size_t)H * e;
+}
+
+size_t swiglu_mlp_bwd_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
+
+int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
+                   int64_t D, int64_t H, int dtype, hipStream_t stream) {
+  size_t e = elt_bytes(dtype);
+  if (!e) return SWIGLU_ERR_DTYPE;
+  int rc = check_shape(T, D, H);
+  if (rc) return rc;
+  Range in[] = {{X, (size_t)T * D * e}, {Wg, (size_t)D * H * e}, {Wu, (size_t)D * H * e}, {Wd, (size_t)H * D * e}};
+  Range out[] = {{Y, (size_t)T * D * e}, {saved, 3 * (size_t)T * H * e}};
+  if ((rc = check_ptrs(in, 4)) || (rc = check_ptrs(out, 2))) return rc;
+  for (auto& o : out)
+    for (auto& i : in)
+      if (overlap(o, i)) return SWIGLU_ERR_ALIAS;
+  if (overlap(out[0], out[1])) return SWIGLU_ERR_ALIAS;
+  if ((rc = check_device())) return rc;
+  if (T == 0) return SWIGLU_OK;
+  switch (dtype) {
+    case SWIGLU_BF16: return run_fwd<Bf16>(X, Wg, Wu, Wd, Y, saved, T, D, H, stream);
+    case SWIGLU_FP16: return run_fwd<Fp16>(X, Wg, Wu, Wd, Y, saved, T, D, H, stream);
+    default: return run_fwd<Fp32>(X, Wg, Wu, Wd, Y, saved, T, D, H, stream);
+  }
+}
+
+int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
+                   void* dX, void* dWg, void* dWu, void* dWd, void* workspace, size_t workspace_bytes, int64_t T,
+                   int64_t D, int64_t H, int dtype, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  size_t e = elt_bytes(dtype);
+  if (!e) return SWIGLU_ERR_DTYPE;
+  int rc = check_shape(T, D, H);
+  if (rc) return rc;
+  const size_t td = (size_t)T * D * e, dh = (size_t)D * H * e;
+  Range in[] = {{dY, td}, {X, td}, {Wg, dh}, {Wu, dh}, {Wd, dh}, {saved, 3 * (size_t)T * H * e}};
+  Range out[] = {{dX, td}, {dWg, dh}, {dWu, dh}, {dWd, dh}};
+  if ((rc = check_ptrs(in, 6)) || (rc = check_ptrs(out, 4))) return rc;
+  for (int i = 0; i < 4; ++i) {
+    for (auto& r : in)
+      if (overlap(out[i], r)) return SWIGLU_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return SWIGLU_ERR_ALIAS;
+  }
+  if ((rc = check_device())) return rc;
+  if (T == 0) {
+    // Sums over zero tokens: the weight gradients are zero; dX is empty.
+    if ((rc = zero_fill(dWg, dh, stream))) return rc;
+    if ((rc = zero_fill(dWu, dh, stream))) return rc;
+    return zero_fill(dWd, dh, stream);
+  }
+  switch (dtype) {
+    case SWIGLU_BF16: return run_bwd<Bf16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, T, D, H, stream);
+    case SWIGLU_FP16: return run_bwd<Fp16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, T, D, H, stream);
+    default: return run_bwd<Fp32>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, T, D, H, stream);
+  }
+}
+
+int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* workspace,
+                     size_t workspace_bytes, int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream) {
+  size_t e = elt_bytes(dtype);
+  if (!e) return SWIGLU_ERR_DTYPE;
+  int rc = check_shape(T, D, H);
+  if (rc) return rc;
+  const size_t need = (size_t)T * H * e;
+  Range in[] = {{X, (size_t)T * D * e}, {Wg, (size_t)D * H * e}, {Wu, (size_t)D * H * e}, {Wd, (size_t)H * D * e}};
+  Range yr[] = {{Y, (size_t)T * D * e}};
+  if ((rc = check_ptrs(in, 4)) || (rc = check_ptrs(yr, 1))) return rc;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return SWIGLU_ERR_ALIGN;
+  Range out[] = {{Y, (size_t)T * D * e}, {workspace, need}};
+  for (auto& o : out)
+    for (auto& i : in)
+      if (overlap(o, i)) return SWIGLU_ERR_ALIAS;
+  if (overlap(out[0], out[1])) return SWIGLU_ERR_ALIAS;
+  if ((rc = check_device())) return rc;
+  if (T == 0) return SWIGLU_OK;
+  switch (dtype) {
+    case SWIGLU_BF16: return run_infer<Bf16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, stream);
+    case SWIGLU_FP16: return run_infer<Fp16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, stream);
+    default: return run_infer<Fp32>(X, Wg, Wu, Wd, Y, workspace, T, D, H, stream);
+  }
+}
+
+const char* swiglu_mlp_status_string(int status) {
+  switch (status) {
+    case SWIGLU_OK: return "ok";
+    case SWIGLU_ERR_NULL: return "a required pointer is NULL";
+    case SWIGLU_ERR_SHAPE: return "bad shape: need T >= 0 and D, H positive multiples of 8";
+    case SWIGLU_ERR_DTYPE: return "unknown dtype";
+    case SWIGLU_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SWIGLU_ERR_ALIAS: return "an output overlaps an input or another output";
+    case SWIGLU_ERR_WORKSPACE: return "workspace missing or too small";
+    case SWIGLU_ERR_DEVICE: return "current device is not gfx950 (or a HIP device query failed)";
+    case SWIGLU_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int swiglu_mlp_timer_start(int capacity) {
+  if (capacity <= 0) return SWIGLU_ERR_SHAPE;
+  for (int s = 0; s < SWIGLU_NUM_STAGES; ++s) {
+    if (g_timer.ev[s]) {
+      for (int i = 0; i < 2 * g_timer.cap; ++i) (void)hipEventDestroy(g_timer.ev[s][i]);
+      delete[] g_timer.ev[s];
+      g_timer.ev[s] = nullptr;
+    }
+  }
+  g_timer.cap = capacity;
+  for (int s = 0; s < SWIGLU_NUM_STAGES; ++s) {
+    g_timer.count[s] = 0;
+    g_timer.ev[s] = new hipEvent_t[2 * capacity];
+    for (int i = 0; i < 2 * capacity; ++i)
+      if (hipEventCreate(&g_timer.ev[s][i]) != hipSuccess) return SWIGLU_ERR_DEVICE;
+  }
+  g_timer.on = true;
+  return SWIGLU_OK;
+}
+
+int swiglu_mlp_timer_stop(double* ms, int* count, int n) {
+  g_timer.on = false;
+  for (int s = 0; s < SWIGLU_NUM_STAGES && s < n; ++s) {
+    double sum = 0.0;
+    for (int i = 0; i < g_timer.count[s]; ++i) {
+      float t = 0.f;
+      if (hipEventSynchronize(g_timer.ev[s][2 * i + 1]) != hipSuccess) return SWIGLU_ERR_DEVICE;
+      if (hipEventElapsedTime(&t, g_timer.ev[s][2 * i], g_timer.ev[s][2 * i + 1]) != hipSuccess)
+        return SWIGLU_ERR_DEVICE;
+      sum += t;
+    }
+    if (ms) ms[s] = sum;
+    if (count) count[s] = g_timer.count[s];
+  }
+  return SWIGLU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+/*
+ * swiglu_mlp.h -- C ABI of the fused SwiGLU MLP library for MI355X (gfx950).
+ *
+ * The operation (page "[RFC] Full-pipeline SwiGLU MLP with forward/backward
+ * co-optimization", Liger-Kernel issue #1347, section "Summary"):
+ *
+ *   forward   G = X Wg, U = X Wu, A = SiLU(G) * U, Y = A Wd
+ *   backward  dA = dY Wd^T (never stored), dU = dA * SiLU(G),
+ *             dG = dA * U * SiLU'(G), dWd = A^T dY,
+ *             [dWg | dWu] = X^T [dG | dU]   (one GEMM),
+ *             dI = [dG | dU] [Wg | Wu]^T    (one accumulator over 2H)
+ *   no-grad   the forward without keeping G and U.
+ *
+ * Shapes and layouts. All matrices are dense and row-major (last index
+ * contiguous): X, Y, dY, dX are [T, D]; Wg, Wu, dWg, dWu are [D, H];
+ * Wd, dWd are [H, D]. All tensors of one call share one dtype. T >= 0 is any
+ * value; D and H must be positive multiples of 8. Every pointer must be
+ * 16-byte aligned; pointers to buffers of zero bytes (T = 0) may be NULL.
+ *
+ * Numerics. bf16/fp16 storage with fp32 accumulation; every stored value is
+ * rounded once (round to nearest even) from fp32. The SwiGLU epilogue is the
+ * one-round program of "Scope one-round FP32 SwiGLU to the exact Qwen3.5
+ * contract" (xorl PR #51, review thread): A = rnd(SiLU(g) * u), evaluated in
+ * fp32 from the stored (rounded) g and u. SWIGLU_FP32 is true IEEE fp32:
+ * fp32 operands enter the matrix cores unrounded (the TF32 issue described
+ * in "[RFC] Testing Methodology for FP32 Convergence Tests on Fused
+ * SwiGLU/dSwiGLU Kernels", Liger-Kernel issue #1383, section "Root Cause").
+ *
+ * Saved buffer. One allocation of swiglu_mlp_saved_bytes() bytes holding three
+ * [T, H] planes in the order A, G, U ("store A, G, and U in one contiguous
+ * buffer", issue #1347, section "Summary"). swiglu_mlp_bwd overwrites the G
+ * and U planes with dG and dU ("overwrite expired G/U storage with dG/dU",
+ * same section), so a saved buffer supports exactly one backward (same page,
+ * section "Known limitations and validation gaps"). The A plane is left
+ * unchanged.
+ *
+ * Ownership and streams. The caller owns every buffer; the library keeps no
+ * per-call state and allocates no device memory in these calls. Work is
+ * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ * calls return before it finishes. Arguments are validated on the host
+ * before anything is launched: a nonzero status means nothing was enqueued,
+ * except SWIGLU_ERR_LAUNCH (a launch failed after validation). NaN and Inf
+ * propagate through the arithmetic; there are no device-side traps.
+ * Gradients are written (beta = 0), not accumulated.
+ */
+#ifndef SWIGLU_MLP_H
+#define SWIGLU_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SWIGLU_BF16 = 0, /* bfloat16 storage, fp32 accumulation */
+  SWIGLU_FP16 = 1, /* float16 storage, fp32 accumulation (issue #1347, "Validation environment") */
+  SWIGLU_FP32 = 2  /* IEEE fp32 storage and products */
+} swiglu_dtype_t;
+
+typedef enum {
+  SWIGLU_OK = 0,
+  SWIGLU_ERR_NULL = 1,      /* a required pointer is NULL */
+  SWIGLU_ERR_SHAPE = 2,     /* T < 0, D or H <= 0 or not a multiple of 8, or a size overflows */
+  SWIGLU_ERR_DTYPE = 3,     /* unknown dtype */
+  SWIGLU_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  SWIGLU_ERR_ALIAS = 5,     /* an output overlaps an input or another output */
+  SWIGLU_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required */
+  SWIGLU_ERR_DEVICE = 7,    /* current device is not gfx950, or a HIP query failed */
+  SWIGLU_ERR_LAUNCH = 8     /* a kernel launch failed (work may be partially enqueued) */
+} swiglu_status_t;
+
+/* Bytes of the saved A|G|U buffer: 3 * T * H * sizeof(dtype). 0 on bad args. */
+size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
+
+/* Bytes of the no-grad workspace: the A plane only, T * H * sizeof(dtype)
+ * ("a dedicated no-grad path that does not save G/U", issue #1347, "Summary";
+ * the page's table "Inference, BF16, B=1" equals A + Y). 0 on bad args. */
+size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
+
+/* Bytes of the backward workspace. Currently always 0 (no split-K fix-up). */
+size_t swiglu_mlp_bwd_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
+
+/* Forward for training. Reads X, Wg, Wu, Wd; writes Y [T, D] and the saved
+ * A|G|U buffer (swiglu_mlp_saved_bytes bytes). Y and saved must not overlap
+ * each other or any input. Kernels: gate/up GEMM with the fused SwiGLU
+ * epilogue, then the down projection. */
+int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd,
+                   void* Y, void* saved, int64_t T, int64_t D, int64_t H,
+                   int dtype, hipStream_t stream);
+
+/* Full backward. Reads dY, X, Wg, Wu, Wd and the saved buffer written by
+ * swiglu_mlp_fwd with the same inputs; writes dX [T, D] (the page's dI),
+ * dWg, dWu [D, H], dWd [H, D]. Consumes the saved buffer: its G and U planes
+ * hold dG and dU afterwards, and a second call on it computes garbage.
+ * workspace may be NULL when swiglu_mlp_bwd_workspace_bytes() is 0. Outputs
+ * must not overlap each other, the inputs, or the saved buffer. */
+int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu,
+                   const void* Wd, void* saved, void* dX, void* dWg, void* dWu,
+                   void* dWd, void* workspace, size_t workspace_bytes,
+                   int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream);
+
+/* No-grad forward: Y [T, D] from X and the weights; G and U are never
+ * stored. workspace holds A (>= swiglu_mlp_infer_workspace_bytes bytes).
+ * Y must not overlap the inputs or the workspace. */
+int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd,
+                     void* Y, void* workspace, size_t workspace_bytes,
+                     int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* swiglu_mlp_status_string(int status);
+
+/* ---- Profiling aid (not part of the computation) -------------------------
+ * Stage ids, one per kernel of the path:
+ *   0 gate/up GEMM + SwiGLU (fwd)      1 down projection (fwd)
+ *   2 dA GEMM + in-place dSwiGLU       3 dWd = A^T dY
+ *   4 [dWg | dWu] = X^T [dG | dU]      5 dI single accumulator
+ *   6 no-grad gate/up (A only)         7 no-grad down projection
+ * swiglu_mlp_timer_start(capacity) makes every later launch of a stage record
+ * a HIP event pair around it on the launch stream, up to `capacity` launches
+ * per stage (events are created here; returns a status). swiglu_mlp_timer_stop
+ * waits for the recorded events and writes, for each of the first `n` stages,
+ * the summed milliseconds to ms[s] and the launch count to count[s], then
+ * disables recording. Not thread-safe; meant for a benchmark's timed loop. */
+#define SWIGLU_NUM_STAGES 8
+int swiglu_mlp_timer_start(int capacity);
+int swiglu_mlp_timer_stop(double* ms, int* count, int n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWIGLU_MLP_H */

@@ -1,0 +1,161 @@
+"""Parity of the HIP path with the fp64 oracle (GPU).
+
+Bounds: normalized L2 <= 1e-2 for bf16/fp16 outputs and gradients, <= 1e-5
+in fp32 mode; the forward SwiGLU epilogue within 1 ulp of the correctly
+rounded SiLU(g)*u of the GPU's own stored g, u. Small shapes exercise ragged
+tails in every dimension; the pages' training shapes run in full; the
+largest one (T = 65536, D = 4096, H = 11008) is checked on sampled rows and
+hidden units in the same launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import WORKLOADS, make_inputs, workload_inputs
+from tests._util import TOL, banner, f64, nl2, run_train, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mlp():
+    import backward_gate_up_amd as m
+
+    return m
+
+
+def _np(inp):
+    return {k: v.float().numpy() for k, v in inp.items()}
+
+
+def _check_full(mlp, inp, fmt, label, check_planes=True):
+    banner(f"{label}: GPU fwd+bwd")
+    out = run_train(mlp, to_dev(inp))
+    f = _np(inp)
+    banner(f"{label}: oracle")
+    ref = O.bwd(f["dY"], f["X"], f["Wg"], f["Wu"], f["Wd"], keep=check_planes)
+    if not check_planes:
+        ref["Y"] = O.fwd(f["X"], f["Wg"], f["Wu"], f["Wd"])["Y"]
+    tol = TOL[fmt]
+    errs = {k: nl2(f64(out[k]), ref[k]) for k in ("Y", "dI", "dWg", "dWu", "dWd")}
+    if check_planes:
+        for k in ("G", "U", "dG", "dU"):
+            errs[k] = nl2(f64(out[k]), ref[k])
+    banner(f"{label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= tol, (label, k, v)
+    # the backward leaves the A plane untouched
+    assert torch.equal(out["A"], out["A_after"])
+    # forward epilogue: A within 1 ulp of rnd(SiLU(g) u) from the stored g, u
+    if fmt != "fp32":
+        a_ref = O.round_to(O.epilogue_fwd(f64(out["G"]), f64(out["U"])), fmt)
+        ulp = O.ulp_distance(f64(out["A"]), a_ref, fmt)
+        assert int(ulp.max()) <= 1, (label, int(ulp.max()))
+    return out, errs
+
+
+@pytest.mark.parametrize("T,D,H", [
+    (1, 64, 64), (3, 64, 128), (127, 256, 384), (129, 512, 264),
+    (300, 1024, 2816), (513, 256, 512), (1000, 384, 648), (777, 136, 200),
+])
+def test_ragged_shapes_bf16(mlp, T, D, H):
+    inp = make_inputs(T, D, H, seed=T + D + H, dtype="bf16")
+    _check_full(mlp, inp, "bf16", f"T={T} D={D} H={H}")
+
+
+def test_workload_T128(mlp):
+    _check_full(mlp, workload_inputs("mlp_1024x2816_T128"), "bf16", "1024x2816 T=128")
+
+
+def test_workload_T16384(mlp):
+    _check_full(mlp, workload_inputs("mlp_1024x2816_T16384"), "bf16", "1024x2816 T=16384")
+
+
+def test_workload_T32768(mlp):
+    _check_full(mlp, workload_inputs("mlp_2048x5632_T32768"), "bf16", "2048x5632 T=32768",
+                check_planes=False)
+
+
+def test_fp32_mode_T4096(mlp):
+    _check_full(mlp, workload_inputs("mlp_2048x5632_T4096_fp32", dtype="fp32"), "fp32",
+                "fp32 2048x5632 T=4096")
+
+
+def test_fp16_T16384(mlp):
+    _check_full(mlp, workload_inputs("mlp_1024x2816_T16384", dtype="fp16"), "fp16",
+                "fp16 1024x2816 T=16384")
+
+
+def test_fp32_and_fp16_ragged(mlp):
+    for fmt in ("fp32", "fp16"):
+        inp = make_inputs(333, 136, 264, seed=5, dtype=fmt)
+        _check_full(mlp, inp, fmt, f"{fmt} T=333 D=136 H=264")
+
+
+def test_headline_T65536_sampled(mlp):
+    """D=4096, H=11008, T=65536: sampled rows of Y and dI, sampled hidden
+    units for dWg, dWu (columns) and dWd (rows), plus the saved planes on the
+    sampled rows."""
+    banner("T=65536: inputs")
+    inp = workload_inputs("mlp_4096x11008_T65536")
+    g = to_dev(inp)
+    banner("T=65536: GPU fwd+bwd")
+    y, saved = mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"])
+    rows = np.array([0, 1, 255, 256, 4097, 33333, 65279, 65535])
+    G_s = saved[1][rows].clone()
+    U_s = saved[2][rows].clone()
+    A_s = saved[0][rows].clone()
+    dx, dwg, dwu, dwd = mlp.bwd(g["dY"], g["X"], g["Wg"], g["Wu"], g["Wd"], saved)
+    torch.cuda.synchronize()
+    del g
+    f = _np(inp)
+    banner("T=65536: oracle rows")
+    r = O.rows(rows, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
+    e = {"Y": nl2(f64(y[rows]), r["Y"]), "dI": nl2(f64(dx[rows]), r["dI"]),
+         "G": nl2(f64(G_s), r["G"]), "U": nl2(f64(U_s), r["U"])}
+    a_ref = O.round_to(O.epilogue_fwd(f64(G_s), f64(U_s)), "bf16")
+    assert int(O.ulp_distance(f64(A_s), a_ref, "bf16").max()) <= 1
+    banner("T=65536: oracle hidden units")
+    hs = np.array([0, 1, 127, 128, 5000, 11007])
+    c = O.cols(hs, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
+    e["dWg"] = nl2(f64(dwg[:, hs]), c["dWg"])
+    e["dWu"] = nl2(f64(dwu[:, hs]), c["dWu"])
+    e["dWd"] = nl2(f64(dwd[hs, :]), c["dWd"])
+    banner("T=65536: " + " ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    for k, v in e.items():
+        assert v <= 1e-2, (k, v)
+
+
+@pytest.mark.parametrize("D,H", [(1024, 2816), (4096, 11008)])
+def test_no_grad_path(mlp, D, H):
+    wts = make_inputs(1, D, H, seed=2024 + D, dtype="bf16", with_dy=False)
+    Wg, Wu, Wd = (wts[k].cuda() for k in ("Wg", "Wu", "Wd"))
+    f = {k: wts[k].float().numpy() for k in ("Wg", "Wu", "Wd")}
+    for S in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        X = make_inputs(S, D, H, seed=S, dtype="bf16", with_dy=False)["X"]
+        y = mlp.infer(X.cuda(), Wg, Wu, Wd)
+        y_train, _ = mlp.fwd(X.cuda(), Wg, Wu, Wd)
+        torch.cuda.synchronize()
+        err = nl2(f64(y), O.infer(X.float().numpy(), f["Wg"], f["Wu"], f["Wd"]))
+        banner(f"infer D={D} S={S}: {err:.2e}")
+        assert err <= 1e-2
+        # same tiles, same order: the no-grad Y equals the training Y bitwise
+        assert torch.equal(y, y_train)
+
+
+def test_zero_tokens(mlp):
+    inp = make_inputs(0, 64, 128, seed=1, dtype="bf16")
+    g = to_dev(inp)
+    y, saved = mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"])
+    assert y.shape == (0, 64) and saved.numel() == 0
+    dwg = torch.full((64, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    dwu = dwg.clone()
+    dwd = torch.full((128, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    dx, dwg, dwu, dwd = mlp.bwd(g["dY"], g["X"], g["Wg"], g["Wu"], g["Wd"], saved,
+                                dwg=dwg, dwu=dwu, dwd=dwd)
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 64)
+    assert not dwg.any() and not dwu.any() and not dwd.any()
+    assert mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"]).shape == (0, 64)
