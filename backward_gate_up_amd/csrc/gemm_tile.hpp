@@ -236,40 +236,67 @@ __device__ __forceinline__ f32x4_t frag32(const char* lds, int ro, int ks, int l
   }
 }
 
-// One LDS stage of MFMA work for a wave. a_rows[i]: row offset in the A tile
-// of m-subtile i; b_rows[j]: row offset in the B tile of n-subtile j.
+// MFMA operands of one K sub-step for a wave: TM fragments of the A tile
+// and TN of the B tile (4 dwords each). A K stage (BK) is NSUB = 4 sub-steps:
+// 16 K per sub-step for 16-bit types (one MFMA), 8 K for fp32 (four MFMAs).
+constexpr int NSUB = 4;
+
 template <class E, int BM, int BN, int AL, int BL, int TM, int TN>
-__device__ __forceinline__ void mma_stage(const char* lds_a, const char* lds_b, const int (&a_rows)[TM],
-                                          const int (&b_rows)[TN], f32x16_t (&acc)[TM][TN], int lane) {
-  if constexpr (E::kBytes == 2) {
+struct Frags {
+  u32x4_t a[TM], b[TN];
+
+  __device__ __forceinline__ void read(const char* lds_a, const char* lds_b, const int (&a_rows)[TM],
+                                       const int (&b_rows)[TN], int ks, int lane) {
+    if constexpr (E::kBytes == 2) {
 #pragma unroll
-    for (int ks = 0; ks < E::kBK / 16; ++ks) {
-      u32x4_t fb[TN], fa[TM];
+      for (int j = 0; j < TN; ++j) b[j] = frag16<E, BN, BL>(lds_b, b_rows[j], ks, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag16<E, BN, BL>(lds_b, b_rows[j], ks, lane);
+      for (int i = 0; i < TM; ++i) a[i] = frag16<E, BM, AL>(lds_a, a_rows[i], ks, lane);
+    } else {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = frag16<E, BM, AL>(lds_a, a_rows[i], ks, lane);
+      for (int j = 0; j < TN; ++j) b[j] = __builtin_bit_cast(u32x4_t, frag32<BN, BL>(lds_b, b_rows[j], ks, lane));
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = __builtin_bit_cast(u32x4_t, frag32<BM, AL>(lds_a, a_rows[i], ks, lane));
+    }
+  }
+
+  // acc[i][j] += P(b[j]) * Q(a[i]): rows of the MFMA result are n, columns m.
+  __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
+    if constexpr (E::kBytes == 2) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = E::mfma(fb[j], fa[i], acc[i][j]);
-    }
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < E::kBK / 8; ++ks) {
-      f32x4_t fb[TN], fa[TM];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag32<BN, BL>(lds_b, b_rows[j], ks, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = frag32<BM, AL>(lds_a, a_rows[i], ks, lane);
+        for (int j = 0; j < TN; ++j) acc[i][j] = E::mfma(b[j], a[i], acc[i][j]);
+    } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[j][s], fa[i][s], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j) {
+            // copy the element out first: bit-casting a vector-element
+            // lvalue directly reads element 0
+            const uint32_t bs = b[j][s], as = a[i][s];
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, bs),
+                                                            __builtin_bit_cast(float, as), acc[i][j], 0, 0, 0);
+          }
     }
+  }
+
+  static constexpr int kMfma = TM * TN * (E::kBytes == 2 ? 1 : 4);
+  static constexpr int kReads = (E::kBytes == 2) ? (TM * (AL == MC ? 2 : 1) + TN * (BL == MC ? 2 : 1))
+                                                 : (TM * (AL == MC ? 4 : 1) + TN * (BL == MC ? 4 : 1));
+};
+
+// Scheduling hint: alternate the sub-step's MFMAs with its LDS traffic so that
+// the matrix pipe never waits behind a burst of DS instructions.
+template <int NMFMA, int NDS>
+__device__ __forceinline__ void interleave_mfma_ds() {
+  constexpr int per = (NDS + NMFMA - 1) / NMFMA;
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x300, per, 0);  // then DS read/write
   }
 }
 

@@ -27,6 +27,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "gemm_tile.hpp"
 #include "../../include/swiglu_mlp.h"
 
@@ -49,7 +51,8 @@ struct KArgs {
 // SiLU and its derivative in fp32 from a stored gate value.
 __device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + expf(-g)); }
 
-template <class E, int BM, int BN, int AL, int BL, int KIND>
+// STAGE only names the kernel (one symbol per stage in profiles).
+template <class E, int BM, int BN, int AL, int BL, int KIND, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mlp_gemm(const KArgs g) {
   using Geo = Geometry<E, BM, BN, AL, BL>;
@@ -123,18 +126,57 @@ mlp_gemm(const KArgs g) {
     if constexpr (KIND == GATEUP) lb1.store(sb, tid, BN / 2);
   };
 
+  // Software pipeline (per K stage kt, LDS stage cur, other stage nxt):
+  //   sub-step 0..3 each issue the MFMAs of one sub-step while the operand
+  //   fragments of the following sub-step are read from LDS; during sub-step
+  //   2 the registers holding tile kt+1 are written to stage nxt; one barrier
+  //   then publishes stage nxt, the global loads of tile kt+2 are issued, and
+  //   sub-step 3 runs while the first fragments of stage nxt are read.
+  // Every LDS stage is read only between the barrier that follows its
+  // writes and the barrier that precedes its next overwrite.
+  using F = Frags<E, BM, BN, AL, BL, TM, TN>;
+  constexpr int NM = F::kMfma, NR = F::kReads;
+  constexpr int NW = TileLoader<E, BM, AL>::PER_THREAD + TileLoader<E, RB, BL, BN>::PER_THREAD *
+                                                             (KIND == GATEUP ? 2 : 1);
+  F f0, f1;
+  // One K stage; ST: write tile kt+1 to the other LDS stage, LD: issue the
+  // global loads of tile kt+2, NX: read the first fragments of tile kt+1.
+  // The flags are compile-time so that the steady-state body has no branch
+  // (branches would split the MFMA/DS interleave into separate blocks).
+  auto body = [&](int kt, auto ST, auto LD, auto NX) {
+    const int cur = kt & 1;
+    const char* sa = smem + cur * Geo::STAGE;
+    const char* sb = sa + Geo::A_BYTES;
+    const char* na = smem + (cur ^ 1) * Geo::STAGE;
+    const char* nb = na + Geo::A_BYTES;
+    f1.read(sa, sb, a_rows, b_rows, 1, lane);
+    f0.mma(acc);
+    interleave_mfma_ds<NM, NR>();
+    f0.read(sa, sb, a_rows, b_rows, 2, lane);
+    f1.mma(acc);
+    interleave_mfma_ds<NM, NR>();
+    f1.read(sa, sb, a_rows, b_rows, 3, lane);
+    if constexpr (decltype(ST)::value) store(cur ^ 1);
+    f0.mma(acc);
+    interleave_mfma_ds<NM, NR + (decltype(ST)::value ? NW : 0)>();
+    if constexpr (decltype(ST)::value) __syncthreads();
+    if constexpr (decltype(LD)::value) load(kt + 2);
+    if constexpr (decltype(NX)::value) f0.read(na, nb, a_rows, b_rows, 0, lane);
+    f1.mma(acc);
+    interleave_mfma_ds<NM, decltype(NX)::value ? NR : 0>();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   if (nk > 0) {
     load(0);
     store(0);
+    if (nk > 1) load(1);
     __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-    const char* sa = smem + cur * Geo::STAGE;
-    mma_stage<E, BM, BN, AL, BL, TM, TN>(sa, sa + Geo::A_BYTES, a_rows, b_rows, acc, lane);
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
+    f0.read(smem, smem + Geo::A_BYTES, a_rows, b_rows, 0, lane);
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) body(kt, T_{}, T_{}, T_{});
+    if (kt + 1 < nk) body(kt++, T_{}, F_{}, T_{});
+    body(kt, F_{}, F_{}, F_{});
   }
 
   // ---- epilogue ----------------------------------------------------------
@@ -266,12 +308,12 @@ static inline Operand opnd(const void* p, int64_t ld, int64_t rows, int64_t k) {
   return Operand{(const char*)p, ld, (int)rows, (int)k};
 }
 
-template <class E, int BM, int BN, int AL, int BL, int KIND>
-static int launch(KArgs a, int grid_z, int stage, hipStream_t stream) {
+template <class E, int BM, int BN, int AL, int BL, int KIND, int STAGE>
+static int launch(KArgs a, int grid_z, hipStream_t stream) {
   const int nb = a.tiles_m * a.tiles_n;
   if (nb <= 0) return SWIGLU_OK;
-  StageScope scope(stage, stream);
-  hipLaunchKernelGGL((mlp_gemm<E, BM, BN, AL, BL, KIND>), dim3(nb, 1, grid_z), dim3(256), 0, stream, a);
+  StageScope scope(STAGE, stream);
+  hipLaunchKernelGGL((mlp_gemm<E, BM, BN, AL, BL, KIND, STAGE>), dim3(nb, 1, grid_z), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
@@ -286,8 +328,9 @@ template <class E>
 struct Path {
   static constexpr int EB = E::kBytes;
 
+  template <int STAGE>
   static int gateup(const void* X, const void* Wg, const void* Wu, char* Ap, char* Gp, char* Up,
-                    int64_t T, int64_t D, int64_t H, bool store_gu, int stage, hipStream_t s) {
+                    int64_t T, int64_t D, int64_t H, bool store_gu, hipStream_t s) {
     KArgs a{};
     a.a0 = opnd(X, D, T, D);
     a.b0 = opnd(Wg, H, H, D);
@@ -302,15 +345,15 @@ struct Path {
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(H, 128);
-      return launch<E, 64, 256, KC, MC, GATEUP>(a, 1, stage, s);
+      return launch<E, 64, 256, KC, MC, GATEUP, STAGE>(a, 1, s);
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(H, 128);
-    return launch<E, 256, 256, KC, MC, GATEUP>(a, 1, stage, s);
+    return launch<E, 256, 256, KC, MC, GATEUP, STAGE>(a, 1, s);
   }
 
-  static int down(const char* Ap, const void* Wd, void* Y, int64_t T, int64_t D, int64_t H, int stage,
-                  hipStream_t s) {
+  template <int STAGE>
+  static int down(const char* Ap, const void* Wd, void* Y, int64_t T, int64_t D, int64_t H, hipStream_t s) {
     KArgs a{};
     a.a0 = opnd(Ap, H, T, H);
     a.b0 = opnd(Wd, D, D, H);
@@ -321,11 +364,11 @@ struct Path {
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(D, 256);
-      return launch<E, 64, 256, KC, MC, PLAIN>(a, 1, stage, s);
+      return launch<E, 64, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(D, 256);
-    return launch<E, 256, 256, KC, MC, PLAIN>(a, 1, stage, s);
+    return launch<E, 256, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
   }
 
   static int dgu(const void* dY, const void* Wd, char* Gp, char* Up, int64_t T, int64_t D, int64_t H,
@@ -341,11 +384,11 @@ struct Path {
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(H, 256);
-      return launch<E, 64, 256, KC, KC, DSWIGLU>(a, 1, 2, s);
+      return launch<E, 64, 256, KC, KC, DSWIGLU, 2>(a, 1, s);
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(H, 256);
-    return launch<E, 256, 256, KC, KC, DSWIGLU>(a, 1, 2, s);
+    return launch<E, 256, 256, KC, KC, DSWIGLU, 2>(a, 1, s);
   }
 
   static int dwd(const char* Ap, const void* dY, void* dWd, int64_t T, int64_t D, int64_t H, hipStream_t s) {
@@ -358,7 +401,7 @@ struct Path {
     a.N = (int)D;
     a.tiles_m = cdiv(H, 256);
     a.tiles_n = cdiv(D, 256);
-    return launch<E, 256, 256, MC, MC, PLAIN>(a, 1, 3, s);
+    return launch<E, 256, 256, MC, MC, PLAIN, 3>(a, 1, s);
   }
 
   static int dwgu(const void* X, const char* dGp, const char* dUp, void* dWg, void* dWu, int64_t T, int64_t D,
@@ -374,7 +417,7 @@ struct Path {
     a.N = (int)H;
     a.tiles_m = cdiv(D, 256);
     a.tiles_n = cdiv(H, 256);
-    return launch<E, 256, 256, MC, MC, PLAIN>(a, 2, 4, s);
+    return launch<E, 256, 256, MC, MC, PLAIN, 4>(a, 2, s);
   }
 
   static int dx(const char* dGp, const char* dUp, const void* Wg, const void* Wu, void* dX, int64_t T, int64_t D,
@@ -391,11 +434,11 @@ struct Path {
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(D, 256);
-      return launch<E, 64, 256, KC, KC, DX>(a, 1, 5, s);
+      return launch<E, 64, 256, KC, KC, DX, 5>(a, 1, s);
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(D, 256);
-    return launch<E, 256, 256, KC, KC, DX>(a, 1, 5, s);
+    return launch<E, 256, 256, KC, KC, DX, 5>(a, 1, s);
   }
 };
 
@@ -460,9 +503,9 @@ static int run_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd
                    int64_t D, int64_t H, hipStream_t s) {
   const size_t plane = (size_t)T * H * E::kBytes;
   char* Ap = (char*)saved;
-  int rc = Path<E>::gateup(X, Wg, Wu, Ap, Ap + plane, Ap + 2 * plane, T, D, H, true, 0, s);
+  int rc = Path<E>::template gateup<0>(X, Wg, Wu, Ap, Ap + plane, Ap + 2 * plane, T, D, H, true, s);
   if (rc) return rc;
-  return Path<E>::down(Ap, Wd, Y, T, D, H, 1, s);
+  return Path<E>::template down<1>(Ap, Wd, Y, T, D, H, s);
 }
 
 template <class E>
@@ -483,9 +526,9 @@ template <class E>
 static int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws, int64_t T,
                      int64_t D, int64_t H, hipStream_t s) {
   char* Ap = (char*)ws;
-  int rc = Path<E>::gateup(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, 6, s);
+  int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, s);
   if (rc) return rc;
-  return Path<E>::down(Ap, Wd, Y, T, D, H, 7, s);
+  return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, s);
 }
 
 }  // namespace swiglu
