@@ -12,9 +12,9 @@ STATUS = {
     4: "SWIGLU_ERR_ALIGN", 5: "SWIGLU_ERR_ALIAS", 6: "SWIGLU_ERR_WORKSPACE",
     7: "SWIGLU_ERR_DEVICE", 8: "SWIGLU_ERR_LAUNCH",
 }
-NUM_STAGES = 8
+NUM_STAGES = 10
 STAGE_NAMES = ("gateup_swiglu", "down_proj", "dgu_inplace", "dwd", "dwgu", "dx",
-               "infer_gateup", "infer_down")
+               "infer_gateup", "infer_down", "dwd+dgu", "dwgu+dx")
 
 _lib = None
 

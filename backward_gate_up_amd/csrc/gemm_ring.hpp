@@ -1,0 +1,173 @@
+// gemm_ring.hpp -- direct-to-LDS, 4-stage pipeline for the 16-bit training
+// GEMMs (256 x 256 output tiles, 4 waves), gfx950.
+//
+// Why: with operands staged through registers, a 256 x 256 x 64 stage can
+// only be fetched one stage (about 1 us) ahead -- the accumulators and the
+// staging registers fill the register file -- and every barrier then waits
+// for the slowest L2 miss. Here global memory is copied straight into LDS by
+// buffer_load ... lds (no registers, no ds_write), into a ring of four 32 KiB
+// stages, three stages ahead of the matrix cores.
+//
+// Stage s of the K loop lives in LDS array (s & 3). Each stage holds the A
+// tile and the B tile (16 KiB each):
+//   K-major (KC) tile: 256 rows x 32 K = 64 B per row; the 16-byte chunk c of
+//     row r sits at chunk c ^ ((r >> 2) & 3), so the 16 rows that one
+//     16-lane group of a ds_read_b128 reads fall on 16 distinct bank quads.
+//   M/N-major (MC) tile: two 128-column sub-tiles of 32 K rows x 256 B; chunk
+//     c (0..15) of K row kr sits at c ^ ((kr & 3) << 2), so the 4 K rows x 4
+//     chunks that 32 lanes of a ds_read_b64_tr_b16 read are distinct.
+// One buffer_load_dwordx4 ... lds writes 1 KiB of consecutive LDS (lane i at
+// M0 + 16 i, measured on the device), so the swizzle is applied on the global
+// side: each lane fetches the logical chunk that belongs at its slot.
+//
+// Synchronisation per stage s: issue the loads of stage s + 3 (into the slot
+// of stage s - 1, which every wave finished reading before the previous
+// barrier); run sub-step 0 of stage s while reading sub-step 1's fragments;
+// wait until this wave's own loads of stage s + 1 have landed (vmcnt counts
+// this wave's loads in issue order), then a barrier publishes stage s + 1 to
+// all waves; run sub-step 1 while reading stage s + 1's first fragments. The
+// barrier only waits for LDS traffic (lgkmcnt), never for the loads still in
+// flight for later stages.
+#pragma once
+#include "gemm_tile.hpp"
+
+namespace swiglu {
+namespace ring {
+
+constexpr int BK = 32;               // K per stage
+constexpr int NST = 4;               // LDS stages
+constexpr int OPB = 256 * BK * 2;    // one operand tile per stage: 16 KiB
+constexpr int STAGE = 2 * OPB;       // 32 KiB
+constexpr int L = 8;                 // loads per wave per stage (4 for A, 4 for B)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ int mc_off(int kr, int col) {
+  const int sub = col >> 7, cc = col & 127;
+  return sub * 8192 + kr * 256 + (((cc >> 3) ^ ((kr & 3) << 2)) << 4) + (cc & 7) * 2;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Barrier that waits for this wave's LDS traffic only (not for loads in
+// flight to later stages); the memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The loads of one operand tile for one stage: this wave issues 4 of the 16
+// 1-KiB pieces (pieces 4w .. 4w+3).
+template <int LAYOUT>
+struct Dma {
+  uint32_t voff[4];
+
+  // Per-tile lane offsets. r0 is the first row (KC) or, for MC, unused here:
+  // MC sub-tiles are positioned through the descriptor.
+  __device__ __forceinline__ void init(const Operand& op, int r0, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave * 4 + j;
+      if constexpr (LAYOUT == KC) {
+        const int r = q * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        voff[j] = (r0 + r < op.rows) ? (uint32_t)(r * (int)op.ld * 2 + c * 16) : kOOB;
+      } else {
+        const int kr = (q & 7) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ ((kr & 3) << 2);
+        voff[j] = (uint32_t)(kr * (int)op.ld * 2 + c * 16);
+      }
+    }
+  }
+
+  // KC: rows [r0, r0 + 256), K columns [k0, k0 + 32) into `tile`.
+  __device__ __forceinline__ void issue_kc(const Operand& op, int r0, int k0, char* tile, int wave, int lane) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(op.base + (int64_t)r0 * op.ld * 2, ((int64_t)(op.rows - r0)) * op.ld * 2);
+    const bool tail = k0 + BK > op.k;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave * 4 + j;
+      uint32_t vo = voff[j];
+      if (tail) {
+        const int r = q * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        if (k0 + c * 8 >= op.k) vo = kOOB;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + q * 1024), 16, vo, k0 * 2, 0, 0);
+    }
+  }
+
+  // MC: sub-tile 0 = columns [c0, c0 + 128) of op0, sub-tile 1 = columns
+  // [c1, c1 + 128) of op1, K rows [k0, k0 + 32). Waves 0-1 fill sub-tile 0,
+  // waves 2-3 sub-tile 1. K rows past op.k fall outside the descriptor
+  // (zeros); columns past the matrix only feed unstored outputs.
+  __device__ __forceinline__ void issue_mc(const Operand& op0, int c0, const Operand& op1, int c1, int k0,
+                                           char* tile, int wave) {
+    const bool second = wave >= 2;
+    const char* base = second ? op1.base : op0.base;
+    const int64_t ld = second ? op1.ld : op0.ld;
+    const int kk = second ? op1.k : op0.k;
+    const int cs = second ? c1 : c0;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(base + (int64_t)k0 * ld * 2 + (int64_t)cs * 2, ((int64_t)(kk - k0)) * ld * 2 - (int64_t)cs * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (wave * 4 + j) * 1024), 16, voff[j], 0, 0, 0);
+  }
+};
+
+// Operand fragment (8 consecutive K of row ro + (lane & 31), K = ks*16 +
+// (lane >> 5)*8 + 0..7) from a ring stage tile.
+template <int LAYOUT>
+__device__ __forceinline__ u32x4_t frag(const char* tile, int ro, int ks, int lane) {
+  if constexpr (LAYOUT == KC) {
+    return *(const u32x4_t*)(tile + kc_off(ro + (lane & 31), ks * 2 + (lane >> 5)));
+  } else {
+    // ds_read_b64_tr_b16 (lane i of each 16-lane block receives element j
+    // from the address of lane 4j + i/4, column i % 4)
+    const int krow = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+    const int col = ro + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off(krow, col)));
+    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off(krow + 4, col)));
+    u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+  }
+}
+
+template <class E, int AL, int BL>
+struct RFrags {
+  u32x4_t a[4], b[4];
+  __device__ __forceinline__ void read(const char* stage, const int (&ar)[4], const int (&br)[4], int ks,
+                                       int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = frag<BL>(stage + OPB, br[j], ks, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = frag<AL>(stage, ar[i], ks, lane);
+  }
+  __device__ __forceinline__ void mma(f32x16_t (&acc)[4][4]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = E::mfma(b[j], a[i], acc[i][j]);
+  }
+  static constexpr int kReads = 4 * (AL == MC ? 2 : 1) + 4 * (BL == MC ? 2 : 1);
+};
+
+// Scheduling hint: alternate MFMAs with LDS reads and the stage's loads.
+template <int NDS, int NVM>
+__device__ __forceinline__ void interleave() {
+  constexpr int pd = (NDS + 15) / 16, pv = (NVM + 15) / 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, pd, 0);
+    if constexpr (pv > 0) __builtin_amdgcn_sched_group_barrier(0x020, pv, 0);
+  }
+}
+
+}  // namespace ring
+}  // namespace swiglu

@@ -16,11 +16,13 @@
 // store in bf16). Accumulation is fp32 throughout.
 //
 // Data movement per K step (BK = 128 bytes of K per row):
-//   global -> registers: raw buffer loads (16 B per lane). Out-of-range
-//     chunks are given an offset past the descriptor's size, so the hardware
-//     returns zeros: ragged M, N and K tails need no separate code path.
+//   global -> registers: raw buffer loads (16 B per lane) at per-lane offsets
+//     fixed for the tile; K advances through the scalar offset or a rebased
+//     descriptor. Out-of-range chunks get an offset past the descriptor's
+//     size, so the hardware returns zeros: ragged M, N and K tails need no
+//     separate loop.
 //   registers -> LDS: KC tiles are stored [row][K] with the 16-byte chunk
-//     index XOR-ed by (row & 7); MC tiles are stored [K][row] with padding.
+//     index XOR-ed by (row >> 1) & 7; MC tiles are stored [K][row] with padding.
 //   LDS -> MFMA operands: KC tiles with ds_read_b128 (8 consecutive K of one
 //     row per lane); MC tiles with ds_read_b64_tr_b16, which transposes 16 x
 //     4 blocks across each group of 16 lanes so that every lane again holds
@@ -128,6 +130,13 @@ struct Geometry {
   static_assert(LDS <= 160 * 1024, "exceeds gfx950 LDS");
 };
 
+// XOR swizzle of the 16-byte chunk index of K-contiguous LDS rows (128 B per
+// row). The LDS serves a 16-byte-per-lane read in groups of 16 lanes over 64
+// banks (256 B); a group reads 16 consecutive rows at one logical chunk, and
+// rows r and r+1 fall in different bank halves, so XOR-ing with (r >> 1) & 7
+// spreads each group over all 16 bank quads.
+__device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 7; }
+
 // Loads of one operand tile (R rows x BK) into registers, and their LDS
 // store. LR is the row count of the LDS tile the rows land in (a tile may be
 // filled from two sources, each supplying R = LR/2 rows at a row offset).
@@ -143,35 +152,54 @@ struct TileLoader {
   static constexpr int CPR = R * EB / 16;  // MC: chunks per K row
 
   u32x4_t v[PER_THREAD];
+  uint32_t voff[PER_THREAD];  // per-lane byte offsets, fixed for the tile
+
+  // Per-tile setup: the byte offset of each of this thread's chunks within a
+  // K stage. KC: rows past the operand get an out-of-range offset (the
+  // hardware returns zeros). MC: columns past the operand read whatever
+  // follows in memory; they only feed output rows/columns that are never
+  // stored, and K rows past the end fall outside the stage's descriptor.
+  __device__ __forceinline__ void init(const Operand& op, int r0, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int c = tid + 256 * i;
+      if constexpr (LAYOUT == KC) {
+        const int r = c >> 3, kc = c & 7;
+        voff[i] = (r0 + r < op.rows) ? (uint32_t)(r * (int)op.ld * EB + kc * 16) : kOOB;
+      } else {
+        const int kr = c / CPR, mc = c % CPR;
+        voff[i] = (uint32_t)(kr * (int)op.ld * EB + mc * 16);
+      }
+    }
+  }
 
   // Global -> registers for K columns [k0, k0 + BK) and rows [r0, r0 + R).
+  // Steady state: no per-lane address arithmetic (KC advances the scalar
+  // offset, MC rebases the descriptor); only a ragged last K stage of a KC
+  // operand masks its chunks.
   __device__ __forceinline__ void load(const Operand& op, int r0, int k0, int tid) {
     if constexpr (LAYOUT == KC) {
-      // rows are K-contiguous: 8 chunks per row (128 bytes of K)
       const char* tb = op.base + (int64_t)r0 * op.ld * EB;
-      int64_t bytes = ((int64_t)(op.rows - r0)) * op.ld * EB;
+      const int64_t bytes = ((int64_t)(op.rows - r0)) * op.ld * EB;
       __amdgpu_buffer_rsrc_t rs = make_rsrc(tb, bytes);
+      const int soff = k0 * EB;
+      if (k0 + BK <= op.k) {
 #pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        int c = tid + 256 * i;
-        int r = c >> 3, kc = c & 7;
-        bool ok = (r0 + r < op.rows) && (k0 + kc * CE < op.k);
-        uint32_t off = (uint32_t)(r * (int)op.ld * EB) + (uint32_t)((k0 + kc * CE) * EB);
-        v[i] = buf_load16(rs, ok ? off : kOOB);
+        for (int i = 0; i < PER_THREAD; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], soff, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+          const int kc = (tid + 256 * i) & 7;
+          const bool ok = k0 + kc * CE < op.k;
+          v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? voff[i] : kOOB, soff, 0);
+        }
       }
     } else {
-      // K rows, each R-contiguous
       const char* tb = op.base + (int64_t)k0 * op.ld * EB + (int64_t)r0 * EB;
-      int64_t bytes = ((int64_t)(op.k - k0)) * op.ld * EB - (int64_t)r0 * EB;
+      const int64_t bytes = ((int64_t)(op.k - k0)) * op.ld * EB - (int64_t)r0 * EB;
       __amdgpu_buffer_rsrc_t rs = make_rsrc(tb, bytes);
 #pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        int c = tid + 256 * i;
-        int kr = c / CPR, mc = c % CPR;
-        bool ok = (k0 + kr < op.k) && (r0 + mc * CE < op.rows);
-        uint32_t off = (uint32_t)(kr * (int)op.ld * EB) + (uint32_t)(mc * 16);
-        v[i] = buf_load16(rs, ok ? off : kOOB);
-      }
+      for (int i = 0; i < PER_THREAD; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, 0);
     }
   }
 
@@ -183,7 +211,7 @@ struct TileLoader {
       int c = tid + 256 * i;
       if constexpr (LAYOUT == KC) {
         int r = row_off + (c >> 3), kc = c & 7;
-        *(u32x4_t*)(lds + r * 128 + ((kc ^ (r & 7)) << 4)) = v[i];
+        *(u32x4_t*)(lds + r * 128 + ((kc ^ kc_swz(r)) << 4)) = v[i];
       } else {
         int kr = c / CPR, mc = c % CPR;
         *(u32x4_t*)(lds + kr * (LR + PAD) * EB + row_off * EB + mc * 16) = v[i];
@@ -200,7 +228,7 @@ __device__ __forceinline__ u32x4_t frag16(const char* lds, int ro, int ks, int l
   if constexpr (LAYOUT == KC) {
     int row = ro + (lane & 31);
     int chunk = ks * 2 + (lane >> 5);
-    return *(const u32x4_t*)(lds + row * 128 + ((chunk ^ (row & 7)) << 4));
+    return *(const u32x4_t*)(lds + row * 128 + ((chunk ^ kc_swz(row)) << 4));
   } else {
     constexpr int PAD = 32;
     constexpr int STRIDE = (R + PAD) * 2;
@@ -226,7 +254,7 @@ __device__ __forceinline__ f32x4_t frag32(const char* lds, int ro, int ks, int l
   if constexpr (LAYOUT == KC) {
     int row = ro + (lane & 31);
     int chunk = ks * 2 + (lane >> 5);
-    return *(const f32x4_t*)(lds + row * 128 + ((chunk ^ (row & 7)) << 4));
+    return *(const f32x4_t*)(lds + row * 128 + ((chunk ^ kc_swz(row)) << 4));
   } else {
     constexpr int STRIDE = (R + 8) * 4;
     int k = ks * 8 + (lane >> 5) * 4;
@@ -304,9 +332,8 @@ __device__ __forceinline__ void interleave_mfma_ds() {
 // are dealt round-robin to the 8 XCDs, each with its own L2; renumber so that
 // each XCD receives a contiguous run of tiles, then walk tiles in groups of
 // 8 M-tiles (M fastest) so that concurrently running tiles share operands.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   int nb = tiles_m * tiles_n;
-  int bid = blockIdx.x;
   int nb8 = nb & ~7;
   if (bid < nb8) bid = (bid & 7) * (nb8 >> 3) + (bid >> 3);
   constexpr int G = 8;

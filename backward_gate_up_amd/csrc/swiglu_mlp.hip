@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "gemm_tile.hpp"
+#include "gemm_ring.hpp"
 #include "../../include/swiglu_mlp.h"
 
 namespace swiglu {
@@ -46,31 +47,142 @@ struct KArgs {
   int M, N;        // output extent (GATEUP: N = H)
   int tiles_m, tiles_n;
   int store_gu;    // GATEUP: write the G and U planes (training) or A only (no-grad)
+  int planes;      // PLAIN: number of (B source, output) planes (1 or 2)
 };
 
-// SiLU and its derivative in fp32 from a stored gate value.
-__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + expf(-g)); }
+// Logistic function sigma(g) = 1 / (1 + exp(-g)) in fp32, from a stored gate
+// value. IEEE form: expf from the device math library and IEEE division
+// (fp32 mode). Fast form (bf16/fp16 storage): exp(-g) = 2^(-g log2 e) with
+// the hardware base-2 exponential, then the hardware reciprocal; both are
+// about 1 fp32 ulp, far below half an ulp of the 16-bit result, so the value
+// rounded to bf16/fp16 is the correctly rounded one except within ~1e-5
+// relative of a rounding tie (then 1 ulp away). For g <= -80 the reciprocal
+// nears the fp32 denormal range, where the hardware approximations flush;
+// those lanes take the IEEE form.
+__device__ __forceinline__ float sigmoid_ieee(float g) { return 1.0f / (1.0f + expf(-g)); }
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  if (g > -80.0f) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+  }
+  return sigmoid_ieee(g);
+}
+template <class E>
+__device__ __forceinline__ float sigmoid_f32(float g) {
+  if constexpr (E::kBytes == 4) return sigmoid_ieee(g);
+  else return sigmoid_fast(g);
+}
 
-// STAGE only names the kernel (one symbol per stage in profiles).
-template <class E, int BM, int BN, int AL, int BL, int KIND, int STAGE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mlp_gemm(const KArgs g) {
+// Epilogue of one tile. acc[i][j][r] holds output
+//   m = m0 + a_rows[i] + (lane & 31),
+//   n = (column base of subtile j) + (r / 4) * 8 + (lane / 32) * 4 + r % 4,
+// so each lane stores runs of 4 consecutive n (8 bytes in bf16).
+template <class E, int BM, int BN, int KIND, int TM, int TN>
+__device__ __forceinline__ void epilogue(const KArgs& g, char* C, f32x16_t (&acc)[TM][TN], int m0, int n0,
+                                         const int (&a_rows)[TM], const int (&b_rows)[TN], int wn, int lane) {
+  constexpr int EB = E::kBytes;
+  using V4 = typename E::vec4;
+  const int ml = lane & 31;
+  const int nl = (lane >> 5) * 4;
+  if constexpr (KIND == GATEUP) {
+    constexpr int H2 = TN / 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + a_rows[i] + ml;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < H2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * (BN / 4) + j * 32 + q * 8 + nl;
+          if (n >= g.N) continue;
+          V4 gv, uv, av;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            typename E::elem gs = E::from_f32(acc[i][j][q * 4 + e]);
+            typename E::elem us = E::from_f32(acc[i][j + H2][q * 4 + e]);
+            float gf = E::to_f32(gs), uf = E::to_f32(us);
+            gv[e] = gs;
+            uv[e] = us;
+            av[e] = E::from_f32(gf * sigmoid_f32<E>(gf) * uf);
+          }
+          const int64_t off = ((int64_t)m * g.ldc + n) * EB;
+          *(V4*)(g.c0 + off) = av;
+          if (g.store_gu) {
+            *(V4*)(g.c1 + off) = gv;
+            *(V4*)(g.c2 + off) = uv;
+          }
+        }
+      }
+    }
+  } else if constexpr (KIND == DSWIGLU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + a_rows[i] + ml;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + b_rows[j] + q * 8 + nl;
+          if (n >= g.N) continue;
+          const int64_t off = ((int64_t)m * g.ldc + n) * EB;
+          V4 gv = *(const V4*)(g.c0 + off);
+          V4 uv = *(const V4*)(g.c1 + off);
+          V4 dg, du;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float da = acc[i][j][q * 4 + e];
+            float gf = E::to_f32(gv[e]), uf = E::to_f32(uv[e]);
+            float s = sigmoid_f32<E>(gf);
+            du[e] = E::from_f32(da * (gf * s));
+            dg[e] = E::from_f32(da * uf * (s * (1.0f + gf * (1.0f - s))));
+          }
+          *(V4*)(g.c0 + off) = dg;
+          *(V4*)(g.c1 + off) = du;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + a_rows[i] + ml;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + b_rows[j] + q * 8 + nl;
+          if (n >= g.N) continue;
+          V4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = E::from_f32(acc[i][j][q * 4 + e]);
+          *(V4*)(C + ((int64_t)m * g.ldc + n) * EB) = v;
+        }
+      }
+    }
+  }
+}
+
+// One output tile: the K loop and the epilogue. bid is the tile's index in
+// its launch group, bz the plane (PLAIN with two B sources / outputs).
+template <class E, int BM, int BN, int AL, int BL, int KIND>
+__device__ __forceinline__ void gemm_tile(const KArgs& g, char* smem, int bid, int bz) {
   using Geo = Geometry<E, BM, BN, AL, BL>;
   constexpr int EB = E::kBytes;
   constexpr int BK = E::kBK;
   constexpr int TM = Geo::TM, TN = Geo::TN;
-  __shared__ __attribute__((aligned(16))) char smem[Geo::LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  tile_coords(g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords(bid, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM;
   const int n0 = (KIND == GATEUP) ? tn * (BN / 2) : tn * BN;
 
   Operand A = g.a0, B = g.b0;
   char* C = g.c0;
-  if (KIND == PLAIN && blockIdx.z == 1) {
+  if (KIND == PLAIN && bz == 1) {
     B = g.b1;
     C = g.c1;
   }
@@ -105,6 +217,14 @@ mlp_gemm(const KArgs g) {
   const int nk1 = (A.k + BK - 1) / BK;
   const int nk = (KIND == DX) ? 2 * nk1 : nk1;
 
+  if constexpr (KIND == DX) {
+    la.init(g.a0, m0, tid);  // both K halves share the layout and extents
+    lb0.init(g.b0, n0, tid);
+  } else {
+    la.init(A, m0, tid);
+    lb0.init(B, n0, tid);
+    if constexpr (KIND == GATEUP) lb1.init(g.b1, n0, tid);
+  }
   auto load = [&](int kt) {
     if constexpr (KIND == DX) {
       bool second = kt >= nk1;
@@ -179,90 +299,176 @@ mlp_gemm(const KArgs g) {
     body(kt, F_{}, F_{}, F_{});
   }
 
-  // ---- epilogue ----------------------------------------------------------
-  // acc[i][j][r]: m = m0 + a_rows[i] + (lane & 31),
-  //               n = (column base of subtile j) + (r / 4) * 8 + (lane / 32) * 4 + r % 4.
-  using V4 = typename E::vec4;
-  const int ml = lane & 31;
-  const int nl = (lane >> 5) * 4;
-  if constexpr (KIND == GATEUP) {
-    constexpr int H2 = TN / 2;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + a_rows[i] + ml;
-      if (m >= g.M) continue;
-#pragma unroll
-      for (int j = 0; j < H2; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * (BN / 4) + j * 32 + q * 8 + nl;
-          if (n >= g.N) continue;
-          V4 gv, uv, av;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            typename E::elem gs = E::from_f32(acc[i][j][q * 4 + e]);
-            typename E::elem us = E::from_f32(acc[i][j + H2][q * 4 + e]);
-            float gf = E::to_f32(gs), uf = E::to_f32(us);
-            gv[e] = gs;
-            uv[e] = us;
-            av[e] = E::from_f32(gf * sigmoid_f32(gf) * uf);
-          }
-          const int64_t off = ((int64_t)m * g.ldc + n) * EB;
-          *(V4*)(g.c0 + off) = av;
-          if (g.store_gu) {
-            *(V4*)(g.c1 + off) = gv;
-            *(V4*)(g.c2 + off) = uv;
-          }
-        }
-      }
-    }
-  } else if constexpr (KIND == DSWIGLU) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + a_rows[i] + ml;
-      if (m >= g.M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + b_rows[j] + q * 8 + nl;
-          if (n >= g.N) continue;
-          const int64_t off = ((int64_t)m * g.ldc + n) * EB;
-          V4 gv = *(const V4*)(g.c0 + off);
-          V4 uv = *(const V4*)(g.c1 + off);
-          V4 dg, du;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float da = acc[i][j][q * 4 + e];
-            float gf = E::to_f32(gv[e]), uf = E::to_f32(uv[e]);
-            float s = sigmoid_f32(gf);
-            du[e] = E::from_f32(da * (gf * s));
-            dg[e] = E::from_f32(da * uf * (s * (1.0f + gf * (1.0f - s))));
-          }
-          *(V4*)(g.c0 + off) = dg;
-          *(V4*)(g.c1 + off) = du;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + a_rows[i] + ml;
-      if (m >= g.M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + b_rows[j] + q * 8 + nl;
-          if (n >= g.N) continue;
-          V4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = E::from_f32(acc[i][j][q * 4 + e]);
-          *(V4*)(C + ((int64_t)m * g.ldc + n) * EB) = v;
-        }
-      }
-    }
+  epilogue<E, BM, BN, KIND, TM, TN>(g, C, acc, m0, n0, a_rows, b_rows, wn, lane);
+}
+
+// One launch = one stage. STAGE only names the kernel (one symbol per
+// stage in profiles). Grid: x = tiles, z = planes.
+template <class E, int BM, int BN, int AL, int BL, int KIND, int STAGE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mlp_gemm(const KArgs g) {
+  __shared__ __attribute__((aligned(16))) char smem[Geometry<E, BM, BN, AL, BL>::LDS];
+  gemm_tile<E, BM, BN, AL, BL, KIND>(g, smem, blockIdx.x, blockIdx.z);
+}
+
+// Two independent stages in one launch: the first group's tiles (g1, with
+// g1.planes planes) take the lowest workgroup ids, so long-K tiles can be
+// dispatched first and the second group's short tiles fill in behind them;
+// this removes the wave-quantization tail of launches with few tiles.
+template <class E, int AL1, int BL1, int KIND1, int AL2, int BL2, int KIND2, int STAGE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mlp_gemm_pair(const KArgs g1, const KArgs g2) {
+  constexpr int L1 = Geometry<E, 256, 256, AL1, BL1>::LDS, L2 = Geometry<E, 256, 256, AL2, BL2>::LDS;
+  __shared__ __attribute__((aligned(16))) char smem[L1 > L2 ? L1 : L2];
+  const int nt1 = g1.tiles_m * g1.tiles_n;
+  const int n1 = nt1 * g1.planes;
+  const int b = blockIdx.x;
+  if (b < n1)
+    gemm_tile<E, 256, 256, AL1, BL1, KIND1>(g1, smem, b % nt1, b / nt1);
+  else
+    gemm_tile<E, 256, 256, AL2, BL2, KIND2>(g2, smem, b - n1, 0);
+}
+
+
+// One 256 x 256 output tile on the direct-to-LDS ring (16-bit types; see
+// gemm_ring.hpp). st0..st3 are the four stage arrays; separate arrays let the
+// compiler wait for exactly the stage a read needs.
+template <class E, int AL, int BL, int KIND>
+__device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, char* st2, char* st3, int bid,
+                                          int bz) {
+  using namespace ring;
+  static_assert(E::kBytes == 2, "the ring pipeline is for bf16/fp16");
+  // the wave index is uniform within a wave; readfirstlane lets the compiler
+  // keep it (and the DMA destinations and descriptors derived from it) in
+  // scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(bid, g.tiles_m, g.tiles_n, tm, tn);
+  const int m0 = tm * 256;
+  const int n0 = (KIND == GATEUP) ? tn * 128 : tn * 256;
+  Operand A = g.a0, B = g.b0;
+  char* C = g.c0;
+  if (KIND == PLAIN && bz == 1) {
+    B = g.b1;
+    C = g.c1;
   }
+  int a_rows[4], b_rows[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_rows[i] = wm * 128 + i * 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b_rows[j] = (KIND == GATEUP) ? (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  Dma<AL> da;
+  Dma<BL> db;
+  da.init(A, m0, wave, lane);
+  db.init(B, n0, wave, lane);
+  const int nk1 = (A.k + BK - 1) / BK;
+  const int nk = (KIND == DX) ? 2 * nk1 : nk1;
+  char* st[4] = {st0, st1, st2, st3};
+
+  auto issue = [&](int s, char* stg) {
+    if constexpr (KIND == DX) {
+      const bool h = s >= nk1;
+      const int k0 = (h ? s - nk1 : s) * BK;
+      da.issue_kc(h ? g.a1 : g.a0, m0, k0, stg, wave, lane);
+      db.issue_kc(h ? g.b1 : g.b0, n0, k0, stg + OPB, wave, lane);
+    } else {
+      const int k0 = s * BK;
+      if constexpr (AL == KC) da.issue_kc(A, m0, k0, stg, wave, lane);
+      else da.issue_mc(A, m0, A, m0 + 128, k0, stg, wave);
+      if constexpr (BL == KC) db.issue_kc(B, n0, k0, stg + OPB, wave, lane);
+      else if constexpr (KIND == GATEUP) db.issue_mc(g.b0, n0, g.b1, n0, k0, stg + OPB, wave);
+      else db.issue_mc(B, n0, B, n0 + 128, k0, stg + OPB, wave);
+    }
+  };
+
+  using F = RFrags<E, AL, BL>;
+  F f0, f1;
+  if (nk > 0) {
+    issue(0, st0);
+    if (nk > 1) issue(1, st1);
+    if (nk > 2) issue(2, st2);
+    if (nk > 2) wait_vmcnt<2 * L>();
+    else if (nk > 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    f0.read(st0, a_rows, b_rows, 0, lane);
+  }
+  // Steady state: four stages per trip with static ring slots, every stage
+  // issuing the loads of stage s + 3 (needs s + 6 < nk for the last one).
+  auto step = [&](int s, auto J) {
+    constexpr int j = decltype(J)::value;
+    issue(s + 3, st[(j + 3) & 3]);
+    f1.read(st[j], a_rows, b_rows, 1, lane);
+    f0.mma(acc);
+    interleave<F::kReads, L>();
+    wait_vmcnt<2 * L>();
+    lds_barrier();
+    f0.read(st[(j + 1) & 3], a_rows, b_rows, 0, lane);
+    f1.mma(acc);
+    interleave<F::kReads, 0>();
+  };
+  int s = 0;
+  for (; s + 7 <= nk; s += 4) {
+    step(s, std::integral_constant<int, 0>{});
+    step(s + 1, std::integral_constant<int, 1>{});
+    step(s + 2, std::integral_constant<int, 2>{});
+    step(s + 3, std::integral_constant<int, 3>{});
+  }
+  // Last stages: same order with run-time slot selection and counts.
+  auto slot = [&](int i) -> char* {
+    i &= 3;
+    return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3;
+  };
+  for (; s < nk; ++s) {
+    if (s + 3 < nk) issue(s + 3, slot(s + 3));
+    f1.read(slot(s), a_rows, b_rows, 1, lane);
+    f0.mma(acc);
+    if (s + 1 < nk) {
+      const int later = nk - (s + 2) < 2 ? nk - (s + 2) : 2;  // stages issued after s + 1
+      if (later >= 2) wait_vmcnt<2 * L>();
+      else if (later == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      f0.read(slot(s + 1), a_rows, b_rows, 0, lane);
+    }
+    f1.mma(acc);
+  }
+  epilogue<E, 256, 256, KIND, 4, 4>(g, C, acc, m0, n0, a_rows, b_rows, wn, lane);
+}
+
+template <class E, int AL, int BL, int KIND, int STAGE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+ring_gemm(const KArgs g) {
+  __shared__ __attribute__((aligned(16))) char s0[ring::STAGE];
+  __shared__ __attribute__((aligned(16))) char s1[ring::STAGE];
+  __shared__ __attribute__((aligned(16))) char s2[ring::STAGE];
+  __shared__ __attribute__((aligned(16))) char s3[ring::STAGE];
+  ring_tile<E, AL, BL, KIND>(g, s0, s1, s2, s3, blockIdx.x, blockIdx.z);
+}
+
+template <class E, int AL1, int BL1, int KIND1, int AL2, int BL2, int KIND2, int STAGE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+ring_gemm_pair(const KArgs g1, const KArgs g2) {
+  __shared__ __attribute__((aligned(16))) char s0[ring::STAGE];
+  __shared__ __attribute__((aligned(16))) char s1[ring::STAGE];
+  __shared__ __attribute__((aligned(16))) char s2[ring::STAGE];
+  __shared__ __attribute__((aligned(16))) char s3[ring::STAGE];
+  const int nt1 = g1.tiles_m * g1.tiles_n;
+  const int n1 = nt1 * g1.planes;
+  const int b = blockIdx.x;
+  if (b < n1)
+    ring_tile<E, AL1, BL1, KIND1>(g1, s0, s1, s2, s3, b % nt1, b / nt1);
+  else
+    ring_tile<E, AL2, BL2, KIND2>(g2, s0, s1, s2, s3, b - n1, 0);
 }
 
 // Fill kernel (used to clear weight gradients when T = 0 would otherwise
@@ -311,9 +517,38 @@ static inline Operand opnd(const void* p, int64_t ld, int64_t rows, int64_t k) {
 template <class E, int BM, int BN, int AL, int BL, int KIND, int STAGE>
 static int launch(KArgs a, int grid_z, hipStream_t stream) {
   const int nb = a.tiles_m * a.tiles_n;
+  a.planes = grid_z;
   if (nb <= 0) return SWIGLU_OK;
   StageScope scope(STAGE, stream);
   hipLaunchKernelGGL((mlp_gemm<E, BM, BN, AL, BL, KIND, STAGE>), dim3(nb, 1, grid_z), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+template <class E, int AL1, int BL1, int K1, int AL2, int BL2, int K2, int STAGE>
+static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
+  const int nb = a1.tiles_m * a1.tiles_n * a1.planes + a2.tiles_m * a2.tiles_n;
+  if (nb <= 0) return SWIGLU_OK;
+  StageScope scope(STAGE, stream);
+  hipLaunchKernelGGL((mlp_gemm_pair<E, AL1, BL1, K1, AL2, BL2, K2, STAGE>), dim3(nb), dim3(256), 0, stream, a1, a2);
+  return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+template <class E, int AL, int BL, int KIND, int STAGE>
+static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
+  const int nb = a.tiles_m * a.tiles_n;
+  a.planes = grid_z;
+  if (nb <= 0) return SWIGLU_OK;
+  StageScope scope(STAGE, stream);
+  hipLaunchKernelGGL((ring_gemm<E, AL, BL, KIND, STAGE>), dim3(nb, 1, grid_z), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+template <class E, int AL1, int BL1, int K1, int AL2, int BL2, int K2, int STAGE>
+static int launch_ring_pair(KArgs a1, KArgs a2, hipStream_t stream) {
+  const int nb = a1.tiles_m * a1.tiles_n * a1.planes + a2.tiles_m * a2.tiles_n;
+  if (nb <= 0) return SWIGLU_OK;
+  StageScope scope(STAGE, stream);
+  hipLaunchKernelGGL((ring_gemm_pair<E, AL1, BL1, K1, AL2, BL2, K2, STAGE>), dim3(nb), dim3(256), 0, stream, a1, a2);
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
@@ -349,7 +584,8 @@ struct Path {
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(H, 128);
-    return launch<E, 256, 256, KC, MC, GATEUP, STAGE>(a, 1, s);
+    if constexpr (E::kBytes == 2) return launch_ring<E, KC, MC, GATEUP, STAGE>(a, 1, s);
+    else return launch<E, 256, 256, KC, MC, GATEUP, STAGE>(a, 1, s);
   }
 
   template <int STAGE>
@@ -368,11 +604,12 @@ struct Path {
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(D, 256);
-    return launch<E, 256, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
+    if constexpr (E::kBytes == 2) return launch_ring<E, KC, MC, PLAIN, STAGE>(a, 1, s);
+    else return launch<E, 256, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
   }
 
-  static int dgu(const void* dY, const void* Wd, char* Gp, char* Up, int64_t T, int64_t D, int64_t H,
-                 hipStream_t s) {
+  // Backward stage arguments (tiles_m/tiles_n filled by the launchers).
+  static KArgs args_dgu(const void* dY, const void* Wd, char* Gp, char* Up, int64_t T, int64_t D, int64_t H) {
     KArgs a{};
     a.a0 = opnd(dY, D, T, D);
     a.b0 = opnd(Wd, D, H, D);  // Bop[k=d][n=h] = Wd[h][d]: K-contiguous rows of Wd
@@ -381,17 +618,10 @@ struct Path {
     a.ldc = H;
     a.M = (int)T;
     a.N = (int)H;
-    if (small_t(T)) {
-      a.tiles_m = cdiv(T, 64);
-      a.tiles_n = cdiv(H, 256);
-      return launch<E, 64, 256, KC, KC, DSWIGLU, 2>(a, 1, s);
-    }
-    a.tiles_m = cdiv(T, 256);
-    a.tiles_n = cdiv(H, 256);
-    return launch<E, 256, 256, KC, KC, DSWIGLU, 2>(a, 1, s);
+    a.planes = 1;
+    return a;
   }
-
-  static int dwd(const char* Ap, const void* dY, void* dWd, int64_t T, int64_t D, int64_t H, hipStream_t s) {
+  static KArgs args_dwd(const char* Ap, const void* dY, void* dWd, int64_t T, int64_t D, int64_t H) {
     KArgs a{};
     a.a0 = opnd(Ap, H, H, T);  // Aop[m=h][k=t] = A[t][h]
     a.b0 = opnd(dY, D, D, T);  // Bop[k=t][n=d] = dY[t][d]
@@ -401,11 +631,11 @@ struct Path {
     a.N = (int)D;
     a.tiles_m = cdiv(H, 256);
     a.tiles_n = cdiv(D, 256);
-    return launch<E, 256, 256, MC, MC, PLAIN, 3>(a, 1, s);
+    a.planes = 1;
+    return a;
   }
-
-  static int dwgu(const void* X, const char* dGp, const char* dUp, void* dWg, void* dWu, int64_t T, int64_t D,
-                  int64_t H, hipStream_t s) {
+  static KArgs args_dwgu(const void* X, const char* dGp, const char* dUp, void* dWg, void* dWu, int64_t T,
+                         int64_t D, int64_t H) {
     KArgs a{};
     a.a0 = opnd(X, D, D, T);    // Aop[m=d][k=t] = X[t][d]
     a.b0 = opnd(dGp, H, H, T);  // Bop[k=t][n=h] = dG[t][h]
@@ -417,11 +647,11 @@ struct Path {
     a.N = (int)H;
     a.tiles_m = cdiv(D, 256);
     a.tiles_n = cdiv(H, 256);
-    return launch<E, 256, 256, MC, MC, PLAIN, 4>(a, 2, s);
+    a.planes = 2;
+    return a;
   }
-
-  static int dx(const char* dGp, const char* dUp, const void* Wg, const void* Wu, void* dX, int64_t T, int64_t D,
-                int64_t H, hipStream_t s) {
+  static KArgs args_dx(const char* dGp, const char* dUp, const void* Wg, const void* Wu, void* dX, int64_t T,
+                       int64_t D, int64_t H) {
     KArgs a{};
     a.a0 = opnd(dGp, H, T, H);
     a.a1 = opnd(dUp, H, T, H);
@@ -431,14 +661,53 @@ struct Path {
     a.ldc = D;
     a.M = (int)T;
     a.N = (int)D;
+    a.planes = 1;
+    return a;
+  }
+
+  // Separate launches (stages 2, 3, 4, 5).
+  static int bwd_separate(KArgs dgu, KArgs dwd, KArgs dwgu, KArgs dx, int64_t T, int64_t D, int64_t H,
+                          hipStream_t s) {
+    int rc;
     if (small_t(T)) {
-      a.tiles_m = cdiv(T, 64);
-      a.tiles_n = cdiv(D, 256);
-      return launch<E, 64, 256, KC, KC, DX, 5>(a, 1, s);
+      dgu.tiles_m = cdiv(T, 64);
+      dgu.tiles_n = cdiv(H, 256);
+      rc = launch<E, 64, 256, KC, KC, DSWIGLU, 2>(dgu, 1, s);
+    } else {
+      dgu.tiles_m = cdiv(T, 256);
+      dgu.tiles_n = cdiv(H, 256);
+      rc = launch<E, 256, 256, KC, KC, DSWIGLU, 2>(dgu, 1, s);
     }
-    a.tiles_m = cdiv(T, 256);
-    a.tiles_n = cdiv(D, 256);
-    return launch<E, 256, 256, KC, KC, DX, 5>(a, 1, s);
+    if (rc) return rc;
+    if ((rc = launch<E, 256, 256, MC, MC, PLAIN, 3>(dwd, 1, s))) return rc;
+    if ((rc = launch<E, 256, 256, MC, MC, PLAIN, 4>(dwgu, 2, s))) return rc;
+    if (small_t(T)) {
+      dx.tiles_m = cdiv(T, 64);
+      dx.tiles_n = cdiv(D, 256);
+      return launch<E, 64, 256, KC, KC, DX, 5>(dx, 1, s);
+    }
+    dx.tiles_m = cdiv(T, 256);
+    dx.tiles_n = cdiv(D, 256);
+    return launch<E, 256, 256, KC, KC, DX, 5>(dx, 1, s);
+  }
+
+  // Paired launches: {dWd (long K = T), dA + dSwiGLU} as stage 8, then
+  // {dWg | dWu (long K = T), dI} as stage 9.
+  static int bwd_paired(KArgs dgu, KArgs dwd, KArgs dwgu, KArgs dx, int64_t T, int64_t D, int64_t H,
+                        hipStream_t s) {
+    dgu.tiles_m = cdiv(T, 256);
+    dgu.tiles_n = cdiv(H, 256);
+    dx.tiles_m = cdiv(T, 256);
+    dx.tiles_n = cdiv(D, 256);
+    if constexpr (E::kBytes == 2) {
+      int rc = launch_ring_pair<E, MC, MC, PLAIN, KC, KC, DSWIGLU, 8>(dwd, dgu, s);
+      if (rc) return rc;
+      return launch_ring_pair<E, MC, MC, PLAIN, KC, KC, DX, 9>(dwgu, dx, s);
+    } else {
+      int rc = launch_pair<E, MC, MC, PLAIN, KC, KC, DSWIGLU, 8>(dwd, dgu, s);
+      if (rc) return rc;
+      return launch_pair<E, MC, MC, PLAIN, KC, KC, DX, 9>(dwgu, dx, s);
+    }
   }
 };
 
@@ -515,11 +784,12 @@ static int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
   char* Ap = (char*)saved;
   char* Gp = Ap + plane;
   char* Up = Ap + 2 * plane;
-  int rc = Path<E>::dgu(dY, Wd, Gp, Up, T, D, H, s);
-  if (rc) return rc;
-  if ((rc = Path<E>::dwd(Ap, dY, dWd, T, D, H, s))) return rc;
-  if ((rc = Path<E>::dwgu(X, Gp, Up, dWg, dWu, T, D, H, s))) return rc;
-  return Path<E>::dx(Gp, Up, Wg, Wu, dX, T, D, H, s);
+  KArgs dgu = Path<E>::args_dgu(dY, Wd, Gp, Up, T, D, H);
+  KArgs dwd = Path<E>::args_dwd(Ap, dY, dWd, T, D, H);
+  KArgs dwgu = Path<E>::args_dwgu(X, Gp, Up, dWg, dWu, T, D, H);
+  KArgs dx = Path<E>::args_dx(Gp, Up, Wg, Wu, dX, T, D, H);
+  if (small_t(T)) return Path<E>::bwd_separate(dgu, dwd, dwgu, dx, T, D, H, s);
+  return Path<E>::bwd_paired(dgu, dwd, dwgu, dx, T, D, H, s);
 }
 
 template <class E>

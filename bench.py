@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0
 
 # Algorithmic FLOPs of each kernel per launch, in units of T*D*H.
 STAGE_FLOPS = {"gateup_swiglu": 4, "down_proj": 2, "dgu_inplace": 2, "dwd": 2, "dwgu": 4, "dx": 4,
-               "infer_gateup": 4, "infer_down": 2}
+               "infer_gateup": 4, "infer_down": 2, "dwd+dgu": 4, "dwgu+dx": 8}
 
 
 def stage_bytes(name, T, D, H, e):
@@ -53,6 +53,8 @@ def stage_bytes(name, T, D, H, e):
         "dx": 2 * TH + 2 * DH + TD,
         "infer_gateup": TD + 2 * DH + TH,
         "infer_down": TH + DH + TD,
+        "dwd+dgu": (TH + TD + DH) + (TD + DH + 4 * TH),
+        "dwgu+dx": (TD + 2 * TH + 2 * DH) + (2 * TH + 2 * DH + TD),
     }[name]
 
 
@@ -120,6 +122,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a plain copy kernel "
+                         "of known traffic, used to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -147,6 +152,15 @@ def main():
     dwu = torch.empty((D, H), dtype=bf, device=dev)
     dwd = torch.empty((H, D), dtype=bf, device=dev)
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     def step():
         mlp.fwd(X, Wg, Wu, Wd, y=y, saved=saved)
         mlp.bwd(dY, X, Wg, Wu, Wd, saved, dx=dx, dwg=dwg, dwu=dwu, dwd=dwd)
@@ -168,7 +182,7 @@ def main():
     tflops = flops / (ms_step * 1e-3) / 1e12
 
     stages = {}
-    for s in ("gateup_swiglu", "down_proj", "dgu_inplace", "dwd", "dwgu", "dx"):
+    for s in STAGE_FLOPS:
         n = st.count[s]
         if n:
             ms = st.ms[s] / n

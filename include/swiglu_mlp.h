@@ -118,13 +118,17 @@ const char* swiglu_mlp_status_string(int status);
  *   2 dA GEMM + in-place dSwiGLU       3 dWd = A^T dY
  *   4 [dWg | dWu] = X^T [dG | dU]      5 dI single accumulator
  *   6 no-grad gate/up (A only)         7 no-grad down projection
+ *   8 stages 3 + 2 in one launch       9 stages 4 + 5 in one launch
+ * (for T > 512 the backward runs as launches 8 and 9: the long-K weight-
+ * gradient tiles are dispatched first and the short tiles of the other stage
+ * fill in behind them.)
  * swiglu_mlp_timer_start(capacity) makes every later launch of a stage record
  * a HIP event pair around it on the launch stream, up to `capacity` launches
  * per stage (events are created here; returns a status). swiglu_mlp_timer_stop
  * waits for the recorded events and writes, for each of the first `n` stages,
  * the summed milliseconds to ms[s] and the launch count to count[s], then
  * disables recording. Not thread-safe; meant for a benchmark's timed loop. */
-#define SWIGLU_NUM_STAGES 8
+#define SWIGLU_NUM_STAGES 10
 int swiglu_mlp_timer_start(int capacity);
 int swiglu_mlp_timer_stop(double* ms, int* count, int n);
 
