@@ -330,6 +330,164 @@ mlp_gemm_pair(const KArgs g1, const KArgs g2) {
 }
 
 
+
+// ---------------------------------------------------------------------------
+// Epilogue of the ring kernels: results go through LDS so that every global
+// access is 16 bytes per lane over whole rows (each store instruction covers
+// full 128-byte lines). Each wave uses its own 32 KiB ring array, so after
+// one barrier (all waves done with the K loop) no further synchronisation is
+// needed: LDS operations of one wave complete in order.
+// A wave's output block is `rows` x W elements (W = 64 or 128); in LDS row r
+// holds W*2 bytes and its 16-byte chunk c sits at chunk c ^ (r % (W/8)).
+// ---------------------------------------------------------------------------
+template <class E, int W>
+struct WaveBlock {
+  static constexpr int NC = W / 8;       // 16-byte chunks per row
+  static constexpr int RB = W * 2;       // bytes per row
+  char* buf;
+  __device__ __forceinline__ int off(int r, int col) const {
+    return r * RB + (((col >> 3) ^ (r & (NC - 1))) << 4) + (col & 7) * 2;
+  }
+  // four consecutive elements at (r, col), col % 4 == 0
+  __device__ __forceinline__ void put4(int r, int col, typename E::vec4 v) const {
+    *(typename E::vec4*)(buf + off(r, col)) = v;
+  }
+  __device__ __forceinline__ typename E::vec4 get4(int r, int col) const {
+    return *(const typename E::vec4*)(buf + off(r, col));
+  }
+  // store rows [0, rows) to dst(row0 + r, col0 + c), masked to M x N
+  __device__ __forceinline__ void store(char* dst, int64_t ld, int row0, int col0, int M, int N, int rows,
+                                        int lane) const {
+    const int n16 = rows * NC;
+#pragma unroll 4
+    for (int g = lane; g < n16; g += 64) {
+      const int r = g / NC, c = g % NC;
+      const u32x4_t v = *(const u32x4_t*)(buf + r * RB + ((c ^ (r & (NC - 1))) << 4));
+      const int gr = row0 + r, gc = col0 + c * 8;
+      if (gr < M && gc < N) *(u32x4_t*)(dst + ((int64_t)gr * ld + gc) * 2) = v;
+    }
+  }
+  // load rows [0, rows) from src(row0 + r, col0 + c) with direct-to-LDS
+  // loads (1 KiB per instruction: RB-byte rows, swizzle applied on the global
+  // side). Rows past M read as zeros; columns past N feed unstored outputs.
+  __device__ __forceinline__ void load(const char* src, int64_t ld, int64_t plane_bytes, int row0, int col0,
+                                       int rows, int lane) const {
+    const char* base = src + ((int64_t)row0 * ld + col0) * 2;
+    const int64_t avail = plane_bytes - ((int64_t)row0 * ld + col0) * 2;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, avail);
+    constexpr int RPI = 1024 / RB;  // rows per instruction
+    const int rl = lane / NC, p = lane % NC;
+#pragma unroll 4
+    for (int t = 0; t < rows / RPI; ++t) {
+      const int r = t * RPI + rl;
+      const int c = p ^ (r & (NC - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ring::lds_void_t*)(buf + t * 1024), 16,
+                                               (uint32_t)(r * (int)ld * 2 + c * 16), 0, 0, 0);
+    }
+  }
+};
+
+template <class E, int KIND>
+__device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t (&acc)[4][4], int m0, int n0,
+                                              int wm, int wn, int lane, char* wbuf) {
+  using V4 = typename E::vec4;
+  const int ml = lane & 31;
+  const int nl = (lane >> 5) * 4;
+  ring::lds_barrier();  // every wave is done reading the K-loop stages
+  if constexpr (KIND == GATEUP) {
+    // wave block: 128 rows (t) x 64 hidden units, planes A, G, U
+    WaveBlock<E, 64> pa{wbuf}, pg{wbuf + 16384};
+    const int r0 = m0 + wm * 128, c0 = n0 + wn * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          V4 gv, av;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            typename E::elem gs = E::from_f32(acc[i][j][q * 4 + e]);
+            typename E::elem us = E::from_f32(acc[i][j + 2][q * 4 + e]);
+            const float gf = E::to_f32(gs), uf = E::to_f32(us);
+            gv[e] = gs;
+            av[e] = E::from_f32(gf * sigmoid_f32<E>(gf) * uf);
+          }
+          pa.put4(i * 32 + ml, j * 32 + q * 8 + nl, av);
+          pg.put4(i * 32 + ml, j * 32 + q * 8 + nl, gv);
+        }
+    pa.store(g.c0, g.ldc, r0, c0, g.M, g.N, 128, lane);
+    if (g.store_gu) {
+      pg.store(g.c1, g.ldc, r0, c0, g.M, g.N, 128, lane);
+      WaveBlock<E, 64> pu{wbuf};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            V4 uv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uv[e] = E::from_f32(acc[i][j + 2][q * 4 + e]);
+            pu.put4(i * 32 + ml, j * 32 + q * 8 + nl, uv);
+          }
+      pu.store(g.c2, g.ldc, r0, c0, g.M, g.N, 128, lane);
+    }
+  } else if constexpr (KIND == DSWIGLU) {
+    // wave block: 128 rows x 128 hidden units, in two halves of 64 rows; the
+    // G and U blocks are loaded into LDS, turned into dG and dU in place
+    // (the same (t, h) block of this tile only), and stored back.
+    WaveBlock<E, 128> pg{wbuf}, pu{wbuf + 16384};
+    const int64_t plane_bytes = (int64_t)g.M * g.ldc * 2;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r0 = m0 + wm * 128 + hf * 64, c0 = n0 + wn * 128;
+      pg.load(g.c0, g.ldc, plane_bytes, r0, c0, 64, lane);
+      pu.load(g.c1, g.ldc, plane_bytes, r0, c0, 64, lane);
+      ring::wait_vmcnt<0>();
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = hf * 2 + ii;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = ii * 32 + ml, c = j * 32 + q * 8 + nl;
+            const V4 gv = pg.get4(r, c), uv = pu.get4(r, c);
+            V4 dg, du;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float da = acc[i][j][q * 4 + e];
+              const float gf = E::to_f32(gv[e]), uf = E::to_f32(uv[e]);
+              const float sg = sigmoid_f32<E>(gf);
+              du[e] = E::from_f32(da * (gf * sg));
+              dg[e] = E::from_f32(da * uf * (sg * (1.0f + gf * (1.0f - sg))));
+            }
+            pg.put4(r, c, dg);
+            pu.put4(r, c, du);
+          }
+      }
+      pg.store(g.c0, g.ldc, r0, c0, g.M, g.N, 64, lane);
+      pu.store(g.c1, g.ldc, r0, c0, g.M, g.N, 64, lane);
+    }
+  } else {
+    // PLAIN / DX: 128 x 128 block of C
+    WaveBlock<E, 128> pc{wbuf};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          V4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = E::from_f32(acc[i][j][q * 4 + e]);
+          pc.put4(i * 32 + ml, j * 32 + q * 8 + nl, v);
+        }
+    pc.store(C, g.ldc, m0 + wm * 128, n0 + wn * 128, g.M, g.N, 128, lane);
+  }
+}
+
 // One 256 x 256 output tile on the direct-to-LDS ring (16-bit types; see
 // gemm_ring.hpp). st0..st3 are the four stage arrays; separate arrays let the
 // compiler wait for exactly the stage a read needs.
@@ -442,7 +600,7 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
     }
     f1.mma(acc);
   }
-  epilogue<E, 256, 256, KIND, 4, 4>(g, C, acc, m0, n0, a_rows, b_rows, wn, lane);
+  ring_epilogue<E, KIND>(g, C, acc, m0, n0, wm, wn, lane, slot(wave));
 }
 
 template <class E, int AL, int BL, int KIND, int STAGE>
