@@ -35,7 +35,10 @@ namespace swiglu {
 namespace ring {
 
 constexpr int BK = 32;               // K per stage
-constexpr int NST = 4;               // LDS stages
+#ifndef SWIGLU_RING_STAGES
+#define SWIGLU_RING_STAGES 4
+#endif
+constexpr int NST = SWIGLU_RING_STAGES;  // LDS stages (loads run NST - 1 stages ahead)
 constexpr int OPB = 256 * BK * 2;    // one operand tile per stage: 16 KiB
 constexpr int STAGE = 2 * OPB;       // 32 KiB
 constexpr int L = 8;                 // loads per wave per stage (4 for A, 4 for B)
@@ -52,6 +55,14 @@ __device__ __forceinline__ int mc_off(int kr, int col) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `later` stages of this wave's loads are still in flight.
+__device__ __forceinline__ void wait_stages(int later) {
+  if (later >= 3) wait_vmcnt<3 * L>();
+  else if (later == 2) wait_vmcnt<2 * L>();
+  else if (later == 1) wait_vmcnt<L>();
+  else wait_vmcnt<0>();
 }
 
 // Barrier that waits for this wave's LDS traffic only (not for loads in

@@ -115,13 +115,102 @@ def cpu_baseline(inp, D, H, target_s):
                       f"{t:.1f} s, numpy float64 BLAS"}
 
 
+def infer_sweep(mlp, torch, dev, reps=20):
+    """No-grad path at B=1, S in {1..256}, D/H in {1024/2816, 4096/11008}: device
+    time per call (HIP events around the call only) with the 256 MB Infinity
+    Cache flushed before every timed call (a 1 GiB fill outside the events), and
+    HBM GB/s from the call's algorithmic bytes 2*(3*D*H + 2*T*D + 2*T*H)."""
+    from synth import INFER_DH, INFER_S, make_inputs
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    out = {}
+    for D, H in INFER_DH:
+        w = make_inputs(1, D, H, seed=77, dtype="bf16", with_dy=False)
+        Wg, Wu, Wd = (w[k].to(dev) for k in ("Wg", "Wu", "Wd"))
+        rows = {}
+        for S in INFER_S:
+            X = make_inputs(S, D, H, seed=S, dtype="bf16", with_dy=False)["X"].to(dev)
+            y = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for a, b in ev:
+                flush.fill_(1)
+                a.record()
+                mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+                b.record()
+            torch.cuda.synchronize()
+            us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+            med = us[len(us) // 2]
+            nbytes = 2 * (3 * D * H + 2 * S * D + 2 * S * H)
+            rows[str(S)] = {"us": round(med, 2), "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                            "frac_hbm": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
+        out[f"{D}x{H}"] = rows
+    del flush
+    return out
+
+
+def ingest_traffic(fetch_csv, write_csv, copy_mib, command):
+    """Turn two rocprofv3 --pmc runs of `bench.py --copy-calibration-mib N`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into profiles/traffic.json.
+    Each counter is scaled by what it reads for the plain copy kernel of known
+    size in the same run (copy: N MiB read + N MiB written), then averaged per
+    launch of each stage (stage = last template argument of the kernel)."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    from backward_gate_up_amd._lib import STAGE_NAMES
+
+    def per_dispatch(path, counter):
+        vals, names = defaultdict(float), {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    k = int(r["Dispatch_Id"])
+                    vals[k] += float(r["Counter_Value"]) * 1024.0
+                    names[k] = r["Kernel_Name"]
+        return vals, names
+
+    known = copy_mib << 20
+    out = {"source_sha256": kernel_source_hash(), "command": command, "kernels": {}}
+    res = {}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        vals, names = per_dispatch(path, counter)
+        copies = [v for k, v in vals.items() if "copyBuffer" in names[k] or "copy" in names[k].lower()]
+        if not copies:
+            raise SystemExit(f"no copy kernel found in {path}")
+        factor = known / copies[0]
+        out[f"{key}_factor"] = round(factor, 4)
+        per_stage = defaultdict(list)
+        for k, v in vals.items():
+            m = re.search(r"(mlp_gemm|ring_gemm|ring_gemm_pair)<.*,\s*(\d+)>\(", names[k])
+            if m:
+                per_stage[STAGE_NAMES[int(m.group(2))]].append(v * factor)
+        res[key] = {st: sum(v) / len(v) for st, v in per_stage.items()}
+    for st in res["fetch"]:
+        f, w = res["fetch"][st], res["write"].get(st, 0.0)
+        out["kernels"][st] = {"fetch_bytes_per_launch": int(f), "write_bytes_per_launch": int(w),
+                              "hbm_bytes_per_launch": int(f + w)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--ingest-traffic":
+        ingest_traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), " ".join(sys.argv[5:]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-infer", action="store_true", help="skip the no-grad (inference) sweep")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known traffic, used to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -220,6 +309,9 @@ def main():
         "stages": stages,
     }
     del g, X, Wg, Wu, Wd, dY, y, saved, dx, dwg, dwu, dwd
+    if not args.no_infer:
+        out["infer"] = {"metric": "no-grad HBM GB/s (B=1, 256 MB cache flushed per call)",
+                        "peak_GBps": PEAK_HBM_GBS, "by_shape": infer_sweep(mlp, torch, dev)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, D, H, args.cpu_seconds)
     print(json.dumps(out), flush=True)
