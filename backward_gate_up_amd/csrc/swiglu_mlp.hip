@@ -31,6 +31,7 @@
 
 #include "gemm_tile.hpp"
 #include "gemm_ring.hpp"
+#include "gemm_skinny.hpp"
 #include "../../include/swiglu_mlp.h"
 
 namespace swiglu {
@@ -629,6 +630,154 @@ ring_gemm_pair(const KArgs g1, const KArgs g2) {
     ring_tile<E, AL2, BL2, KIND2>(g2, s0, s1, s2, s3, b - n1, 0);
 }
 
+
+// ---------------------------------------------------------------------------
+// Few-token kernels (T <= 64; gemm_skinny.hpp). KIND GATEUP: unit = 16 hidden
+// units, computes G and U for them and writes A (and G, U when store_gu).
+// KIND PLAIN: unit = 16 output columns of C = A_op * B.
+// g.a0: activations [T, K] (K-contiguous); g.b0 (g.b1): weights [K, N]
+// (N-contiguous). MT = number of 16-row token tiles (T <= 16 * MT).
+// ---------------------------------------------------------------------------
+template <class E, int KIND, int MT>
+__device__ __forceinline__ void skinny_unit(const KArgs& g, char* lds, int unit) {
+  using namespace skinny;
+  constexpr int NW = (KIND == GATEUP) ? 2 : 1;  // weight matrices streamed
+  constexpr int C = NW + MT;                    // 1-KiB loads per step
+  constexpr int SLOT = C * 1024;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = unit * 16;
+  const Operand& X = g.a0;
+  const int K = X.k;
+  const int steps = (K + KS - 1) / KS;
+  const int per = (steps + WAVES - 1) / WAVES;
+  const int sbeg = wave * per;
+  const int nst = steps - sbeg < per ? (steps - sbeg > 0 ? steps - sbeg : 0) : per;
+
+  char* ring = lds + wave * NS * SLOT;  // this wave's NS slots
+  const uint32_t ring_addr = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  const int64_t ldw = g.b0.ld;
+  const i32x4_t rw0 = rsrc_words(g.b0.base, (int64_t)K * ldw * 2);
+  const i32x4_t rw1 = rsrc_words(NW == 2 ? g.b1.base : g.b0.base, (int64_t)K * ldw * 2);
+  const i32x4_t rx = rsrc_words(X.base, (int64_t)X.rows * X.ld * 2);
+  // weight slab: lane -> (K row lane / 2, columns n0 + 8 (lane % 2) .. + 7)
+  const uint32_t voff_w = (uint32_t)((lane >> 1) * (int)ldw * 2 + (n0 + (lane & 1) * 8) * 2);
+  // activation tile: lane -> (token row lane / 4, logical chunk of its slot)
+  const int am = lane >> 2;
+  const int ac = (lane & 3) ^ ((am >> 2) & 3);
+
+  auto issue = [&](int i, int sl) {
+    // the slot being refilled was read by this wave one step earlier; make
+    // sure those LDS reads have completed before the new data can land
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const bool live = i < nst;
+    const int k0 = (sbeg + i) * KS;
+    const uint32_t base = ring_addr + sl * SLOT;
+    const uint32_t soff = live ? (uint32_t)(k0 * (int)ldw * 2) : 0u;
+    dma16(base, rw0, live ? voff_w : kOOB, soff);
+    if constexpr (NW == 2) dma16(base + 1024, rw1, live ? voff_w : kOOB, soff);
+    const int k = k0 + ac * 8;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int m = t * 16 + am;
+      const bool ok = live && k < K && m < X.rows;
+      dma16(base + (NW + t) * 1024, rx, ok ? (uint32_t)((m * K + k) * 2) : kOOB, 0u);
+    }
+  };
+
+  f32x4_t acc[NW][MT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4_t{};
+
+  // NS - 1 steps in flight. Step i reads slot i % NS after waiting for its
+  // loads (the NS - 2 later steps' loads may still be in flight), then issues
+  // step i + NS - 1 into the slot read at step i - 1 (those reads completed:
+  // their values fed step i - 1's MFMAs).
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p, p);
+  for (int i = 0; i < nst; i += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      ring::wait_vmcnt<(NS - 2) * C>();
+      const char* sl = ring + j * SLOT;
+      u32x4_t p[NW], qv[MT];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) p[w] = slab_frag(sl + w * 1024, lane);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) qv[t] = act_frag(sl + (NW + t) * 1024, lane);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[w][t] = mfma16<E>(p[w], qv[t], acc[w][t]);
+      issue(i + j + NS - 1, (j + NS - 1) % NS);
+    }
+  }
+  ring::wait_vmcnt<0>();  // the surplus steps' loads (zeros) have landed too
+
+  // sum the four waves' partials through LDS
+  ring::lds_barrier();
+  char* part = lds + wave * (NW * MT * 1024);
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) *(f32x4_t*)(part + ((w * MT + t) * 64 + lane) * 16) = acc[w][t];
+  ring::lds_barrier();
+
+  using V4 = typename E::vec4;
+  const int ncol = n0 + (lane >> 4) * 4;  // 4 consecutive output columns
+  for (int t = wave; t < MT; t += WAVES) {
+    f32x4_t sum[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      sum[w] = f32x4_t{};
+#pragma unroll
+      for (int v = 0; v < WAVES; ++v)
+        sum[w] += *(const f32x4_t*)(lds + v * (NW * MT * 1024) + ((w * MT + t) * 64 + lane) * 16);
+    }
+    const int m = t * 16 + (lane & 15);
+    if (m >= g.M || ncol >= g.N) continue;
+    const int64_t off = ((int64_t)m * g.ldc + ncol) * E::kBytes;
+    if constexpr (KIND == GATEUP) {
+      V4 gv, uv, av;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        typename E::elem gs = E::from_f32(sum[0][e]);
+        typename E::elem us = E::from_f32(sum[1][e]);
+        const float gf = E::to_f32(gs), uf = E::to_f32(us);
+        gv[e] = gs;
+        uv[e] = us;
+        av[e] = E::from_f32(gf * sigmoid_f32<E>(gf) * uf);
+      }
+      *(V4*)(g.c0 + off) = av;
+      if (g.store_gu) {
+        *(V4*)(g.c1 + off) = gv;
+        *(V4*)(g.c2 + off) = uv;
+      }
+    } else {
+      V4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = E::from_f32(sum[0][e]);
+      *(V4*)(g.c0 + off) = v;
+    }
+  }
+}
+
+template <class E, int KIND, int MT, int STAGE>
+__global__ void __launch_bounds__(256) skinny_gemm(const KArgs g) {
+  constexpr int NW = (KIND == GATEUP) ? 2 : 1;
+  constexpr int BYTES = skinny::WAVES * skinny::NS * (NW + MT) * 1024;
+  static_assert(BYTES >= skinny::WAVES * NW * MT * 1024, "partial sums must fit");
+  __shared__ __attribute__((aligned(1024))) char lds[BYTES];
+  // consecutive units on one XCD (the hardware deals workgroups round-robin
+  // over the 8 XCDs)
+  const int nb = gridDim.x, nb8 = nb & ~7;
+  int b = blockIdx.x;
+  if (b < nb8) b = (b & 7) * (nb8 >> 3) + (b >> 3);
+  skinny_unit<E, KIND, MT>(g, lds, b);
+}
+
 // Fill kernel (used to clear weight gradients when T = 0 would otherwise
 // leave them unwritten; a kernel rather than a memset so that callers may
 // capture the path in a graph).
@@ -712,6 +861,24 @@ static int launch_ring_pair(KArgs a1, KArgs a2, hipStream_t stream) {
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// Few-token launch: one workgroup per 16 output columns.
+template <class E, int KIND, int STAGE>
+static int launch_skinny(KArgs a, int64_t T, int64_t ncols, hipStream_t stream) {
+  const int nb = cdiv(ncols, 16);
+  if (nb <= 0 || T <= 0) return SWIGLU_OK;
+  StageScope scope(STAGE, stream);
+  if (T <= 16)
+    hipLaunchKernelGGL((skinny_gemm<E, KIND, 1, STAGE>), dim3(nb), dim3(256), 0, stream, a);
+  else if (T <= 32)
+    hipLaunchKernelGGL((skinny_gemm<E, KIND, 2, STAGE>), dim3(nb), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((skinny_gemm<E, KIND, 4, STAGE>), dim3(nb), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+// Tokens up to which the forward runs on the weight-streaming kernels.
+static inline bool few_t(int64_t T) { return T <= 64; }
+
 // Rows of X per workgroup tile for the T-indexed GEMMs. Small token counts
 // (the no-grad shapes) use short tiles so that more workgroups share the
 // weight stream.
@@ -735,6 +902,8 @@ struct Path {
     a.M = (int)T;
     a.N = (int)H;
     a.store_gu = store_gu ? 1 : 0;
+    if constexpr (E::kBytes == 2)
+      if (few_t(T)) return launch_skinny<E, GATEUP, STAGE>(a, T, H, s);
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(H, 128);
@@ -755,6 +924,8 @@ struct Path {
     a.ldc = D;
     a.M = (int)T;
     a.N = (int)D;
+    if constexpr (E::kBytes == 2)
+      if (few_t(T)) return launch_skinny<E, PLAIN, STAGE>(a, T, D, s);
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(D, 256);
