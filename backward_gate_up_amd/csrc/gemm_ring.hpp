@@ -34,7 +34,7 @@
 namespace swiglu {
 namespace ring {
 
-constexpr int BK = 32;               // K per stage
+constexpr int BK = 32;               // K per stage of the four-stage ring
 #ifndef SWIGLU_RING_STAGES
 #define SWIGLU_RING_STAGES 4
 #endif
@@ -45,11 +45,35 @@ constexpr int L = 8;                 // loads per wave per stage (4 for A, 4 for
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// Geometry of one 256-row (KC) or 256-column (MC) operand tile holding BKT
+// values of K.
+template <int BKT>
+struct Geo {
+  static_assert(BKT == 32 || BKT == 64, "stage depth");
+  static constexpr int ROWB = BKT * 2;            // bytes of a K-major row
+  static constexpr int LPR = ROWB / 16;           // lanes per K-major row in one load
+  static constexpr int RPI = 64 / LPR;            // K-major rows per 1-KiB load
+  static constexpr int OPB = 256 * ROWB;          // bytes per operand tile
+  static constexpr int PPW = OPB / 1024 / 4;      // 1-KiB loads per wave and operand
+  static constexpr int SUB = OPB / 2;             // MC: bytes per 128-column sub-tile
+};
 
+// K-major tile: chunk c of row r. 64-byte rows: c ^ ((r >> 2) & 3); 128-byte
+// rows: c ^ ((r >> 1) & 7). Either way the 16 rows read by one 16-lane group
+// of a ds_read_b128 land on distinct bank quads.
+template <int BKT>
+__device__ __forceinline__ int kc_swz(int r) {
+  return BKT == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+template <int BKT>
+__device__ __forceinline__ int kc_off(int r, int c) {
+  return r * Geo<BKT>::ROWB + ((c ^ kc_swz<BKT>(r)) << 4);
+}
+
+template <int BKT>
 __device__ __forceinline__ int mc_off(int kr, int col) {
   const int sub = col >> 7, cc = col & 127;
-  return sub * 8192 + kr * 256 + (((cc >> 3) ^ ((kr & 3) << 2)) << 4) + (cc & 7) * 2;
+  return sub * Geo<BKT>::SUB + kr * 256 + (((cc >> 3) ^ ((kr & 3) << 2)) << 4) + (cc & 7) * 2;
 }
 
 template <int N>
@@ -57,55 +81,50 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Wait until at most `later` stages of this wave's loads are still in flight.
-__device__ __forceinline__ void wait_stages(int later) {
-  if (later >= 3) wait_vmcnt<3 * L>();
-  else if (later == 2) wait_vmcnt<2 * L>();
-  else if (later == 1) wait_vmcnt<L>();
-  else wait_vmcnt<0>();
-}
-
 // Barrier that waits for this wave's LDS traffic only (not for loads in
 // flight to later stages); the memory clobber keeps the compiler from moving
 // LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// The loads of one operand tile for one stage: this wave issues 4 of the 16
-// 1-KiB pieces (pieces 4w .. 4w+3).
-template <int LAYOUT>
+// The loads of one operand tile for one stage: this wave issues PPW of the
+// 1-KiB pieces (pieces PPW*w .. PPW*w + PPW - 1).
+template <int LAYOUT, int BKT = BK>
 struct Dma {
-  uint32_t voff[4];
+  using G = Geo<BKT>;
+  uint32_t voff[G::PPW];
 
   // Per-tile lane offsets. r0 is the first row (KC) or, for MC, unused here:
   // MC sub-tiles are positioned through the descriptor.
   __device__ __forceinline__ void init(const Operand& op, int r0, int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = wave * 4 + j;
+    for (int j = 0; j < G::PPW; ++j) {
       if constexpr (LAYOUT == KC) {
-        const int r = q * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        const int r = (wave * G::PPW + j) * G::RPI + lane / G::LPR;
+        const int c = (lane % G::LPR) ^ kc_swz<BKT>(r);
         voff[j] = (r0 + r < op.rows) ? (uint32_t)(r * (int)op.ld * 2 + c * 16) : kOOB;
       } else {
-        const int kr = (q & 7) * 4 + (lane >> 4);
+        const int kr = ((wave & 1) * G::PPW + j) * 4 + (lane >> 4);
         const int c = (lane & 15) ^ ((kr & 3) << 2);
         voff[j] = (uint32_t)(kr * (int)op.ld * 2 + c * 16);
       }
     }
   }
 
-  // KC: rows [r0, r0 + 256), K columns [k0, k0 + 32) into `tile`.
-  __device__ __forceinline__ void issue_kc(const Operand& op, int r0, int k0, char* tile, int wave, int lane) {
+  // KC: rows [r0, r0 + 256), K columns [k0, k0 + BKT) into `tile`; this
+  // wave's pieces j0 .. j1 - 1.
+  __device__ __forceinline__ void issue_kc(const Operand& op, int r0, int k0, char* tile, int wave, int lane,
+                                           int j0 = 0, int j1 = G::PPW) {
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(op.base + (int64_t)r0 * op.ld * 2, ((int64_t)(op.rows - r0)) * op.ld * 2);
-    const bool tail = k0 + BK > op.k;
+    const bool tail = k0 + BKT > op.k;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = wave * 4 + j;
+    for (int j = 0; j < G::PPW; ++j) {
+      if (j < j0 || j >= j1) continue;
+      const int q = wave * G::PPW + j;
       uint32_t vo = voff[j];
       if (tail) {
-        const int r = q * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        const int r = q * G::RPI + lane / G::LPR;
+        const int c = (lane % G::LPR) ^ kc_swz<BKT>(r);
         if (k0 + c * 8 >= op.k) vo = kOOB;
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + q * 1024), 16, vo, k0 * 2, 0, 0);
@@ -113,11 +132,11 @@ struct Dma {
   }
 
   // MC: sub-tile 0 = columns [c0, c0 + 128) of op0, sub-tile 1 = columns
-  // [c1, c1 + 128) of op1, K rows [k0, k0 + 32). Waves 0-1 fill sub-tile 0,
+  // [c1, c1 + 128) of op1, K rows [k0, k0 + BKT). Waves 0-1 fill sub-tile 0,
   // waves 2-3 sub-tile 1. K rows past op.k fall outside the descriptor
   // (zeros); columns past the matrix only feed unstored outputs.
   __device__ __forceinline__ void issue_mc(const Operand& op0, int c0, const Operand& op1, int c1, int k0,
-                                           char* tile, int wave) {
+                                           char* tile, int wave, int j0 = 0, int j1 = G::PPW) {
     const bool second = wave >= 2;
     const char* base = second ? op1.base : op0.base;
     const int64_t ld = second ? op1.ld : op0.ld;
@@ -126,38 +145,46 @@ struct Dma {
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(base + (int64_t)k0 * ld * 2 + (int64_t)cs * 2, ((int64_t)(kk - k0)) * ld * 2 - (int64_t)cs * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (wave * 4 + j) * 1024), 16, voff[j], 0, 0, 0);
+    for (int j = 0; j < G::PPW; ++j) {
+      if (j < j0 || j >= j1) continue;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (wave * G::PPW + j) * 1024), 16, voff[j],
+                                               0, 0, 0);
+    }
   }
 };
 
 // Operand fragment (8 consecutive K of row ro + (lane & 31), K = ks*16 +
 // (lane >> 5)*8 + 0..7) from a ring stage tile.
-template <int LAYOUT>
+template <int LAYOUT, int BKT = BK>
 __device__ __forceinline__ u32x4_t frag(const char* tile, int ro, int ks, int lane) {
   if constexpr (LAYOUT == KC) {
-    return *(const u32x4_t*)(tile + kc_off(ro + (lane & 31), ks * 2 + (lane >> 5)));
+    return *(const u32x4_t*)(tile + kc_off<BKT>(ro + (lane & 31), ks * 2 + (lane >> 5)));
   } else {
     // ds_read_b64_tr_b16 (lane i of each 16-lane block receives element j
     // from the address of lane 4j + i/4, column i % 4)
     const int krow = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
     const int col = ro + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off(krow, col)));
-    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off(krow + 4, col)));
+    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off<BKT>(krow, col)));
+    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off<BKT>(krow + 4, col)));
     u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
     return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
   }
 }
 
-template <class E, int AL, int BL>
+template <class E, int AL, int BL, int BKT = BK>
 struct RFrags {
   u32x4_t a[4], b[4];
+  // A tile at `at`, B tile at `bt`
+  __device__ __forceinline__ void read(const char* at, const char* bt, const int (&ar)[4], const int (&br)[4],
+                                       int ks, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = frag<BL, BKT>(bt, br[j], ks, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = frag<AL, BKT>(at, ar[i], ks, lane);
+  }
   __device__ __forceinline__ void read(const char* stage, const int (&ar)[4], const int (&br)[4], int ks,
                                        int lane) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = frag<BL>(stage + OPB, br[j], ks, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = frag<AL>(stage, ar[i], ks, lane);
+    read(stage, stage + Geo<BKT>::OPB, ar, br, ks, lane);
   }
   __device__ __forceinline__ void mma(f32x16_t (&acc)[4][4]) const {
 #pragma unroll
@@ -168,15 +195,22 @@ struct RFrags {
   static constexpr int kReads = 4 * (AL == MC ? 2 : 1) + 4 * (BL == MC ? 2 : 1);
 };
 
-// Scheduling hint: alternate MFMAs with LDS reads and the stage's loads.
+// Scheduling hint for one sub-step of 16 MFMAs: each MFMA is followed by its
+// share of the next sub-step's LDS reads, and the NVM loads are spaced evenly
+// (one after every 16/NVM-th MFMA). All four waves reach this point together
+// after a barrier; issuing a stage's loads back to back would queue 4 x 8
+// loads at the texture unit at once and stall the MFMA issue behind them.
 template <int NDS, int NVM>
 __device__ __forceinline__ void interleave() {
-  constexpr int pd = (NDS + 15) / 16, pv = (NVM + 15) / 16;
+  constexpr int pd = (NDS + 15) / 16;
+  static_assert(NVM == 0 || (NVM <= 16 && 16 % NVM == 0), "loads per sub-step");
+  constexpr int every = NVM > 0 ? 16 / NVM : 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, pd, 0);
-    if constexpr (pv > 0) __builtin_amdgcn_sched_group_barrier(0x020, pv, 0);
+    if constexpr (NVM > 0)
+      if (i % every == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 }
 

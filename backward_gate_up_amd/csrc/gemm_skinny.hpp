@@ -55,28 +55,6 @@ __device__ __forceinline__ u32x4_t slab_frag(const char* slab, int lane) {
   return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
 }
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor words (base, 16 address bits | stride 0, size, flags).
-__device__ __forceinline__ i32x4_t rsrc_words(const void* p, int64_t bytes) {
-  const uint64_t b = (uint64_t)p;
-  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
-  return i32x4_t{(int)(uint32_t)b, (int)((b >> 32) & 0xffff), n, kRsrcWord3};
-}
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
-}
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 lane
-// (lds is wave-uniform).
-__device__ __forceinline__ void dma16(uint32_t lds, i32x4_t rs, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds), "v"(voff), "s"(rs), "s"(soff)
-               : "memory");
-}
-
 // Activation tile in LDS: 16 tokens x 32 K (64 B per token); the 16-byte
 // chunk c of token row m sits at chunk c ^ ((m >> 2) & 3) so that the 16
 // rows one 16-lane group reads fall on distinct bank quads.

@@ -99,6 +99,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcWord3);
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words (base, 16 address bits | stride 0, size, flags)
+// for loads issued from inline assembly.
+__device__ __forceinline__ i32x4_t rsrc_words(const void* p, int64_t bytes) {
+  const uint64_t b = (uint64_t)p;
+  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+  return i32x4_t{(int)(uint32_t)b, (int)((b >> 32) & 0xffff), n, kRsrcWord3};
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// Direct-to-LDS load of 16 bytes per lane from buffer offset voff + soff to
+// LDS address lds + 16 * lane (lds is wave-uniform). Issued from inline
+// assembly, the compiler neither sees the LDS write nor waits for it: the
+// caller waits (s_waitcnt vmcnt counts this wave's loads in issue order) and
+// publishes with a barrier. The memory clobber keeps other memory accesses
+// on their side of it.
+__device__ __forceinline__ void dma16(uint32_t lds, i32x4_t rs, uint32_t voff, uint32_t soff) {
+  // wave-uniform by contract; readfirstlane keeps them in scalar registers
+  // where the compiler could not prove it
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rs), "s"(soff)
+               : "memory");
+}
+
 __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -331,12 +362,12 @@ __device__ __forceinline__ void interleave_mfma_ds() {
 // Map the workgroup id to a (tile_m, tile_n) pair. Consecutive workgroup ids
 // are dealt round-robin to the 8 XCDs, each with its own L2; renumber so that
 // each XCD receives a contiguous run of tiles, then walk tiles in groups of
-// 8 M-tiles (M fastest) so that concurrently running tiles share operands.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// G M-tiles (M fastest) so that concurrently running tiles share operands:
+// the 32 tiles an XCD runs at once cover G M-tiles x 32/G N-tiles.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int G, int& tm, int& tn) {
   int nb = tiles_m * tiles_n;
   int nb8 = nb & ~7;
   if (bid < nb8) bid = (bid & 7) * (nb8 >> 3) + (bid >> 3);
-  constexpr int G = 8;
   int group = bid / (G * tiles_n);
   int first_m = group * G;
   int gm = tiles_m - first_m < G ? tiles_m - first_m : G;

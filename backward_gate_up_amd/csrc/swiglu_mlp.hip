@@ -49,6 +49,7 @@ struct KArgs {
   int tiles_m, tiles_n;
   int store_gu;    // GATEUP: write the G and U planes (training) or A only (no-grad)
   int planes;      // PLAIN: number of (B source, output) planes (1 or 2)
+  int group_m;     // M-tiles per group of the tile walk (tile_coords); 0 = 8
 };
 
 // Logistic function sigma(g) = 1 / (1 + exp(-g)) in fp32, from a stored gate
@@ -177,7 +178,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, char* smem, int bid, i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  tile_coords(bid, g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords(bid, g.tiles_m, g.tiles_n, g.group_m > 0 ? g.group_m : 8, tm, tn);
   const int m0 = tm * BM;
   const int n0 = (KIND == GATEUP) ? tn * (BN / 2) : tn * BN;
 
@@ -503,7 +504,7 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  tile_coords(bid, g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords(bid, g.tiles_m, g.tiles_n, g.group_m > 0 ? g.group_m : 8, tm, tn);
   const int m0 = tm * 256;
   const int n0 = (KIND == GATEUP) ? tn * 128 : tn * 256;
   Operand A = g.a0, B = g.b0;
@@ -533,20 +534,31 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   const int nk = (KIND == DX) ? 2 * nk1 : nk1;
   char* st[4] = {st0, st1, st2, st3};
 
-  auto issue = [&](int s, char* stg) {
+  auto issue_a = [&](int s, char* stg) {
     if constexpr (KIND == DX) {
       const bool h = s >= nk1;
-      const int k0 = (h ? s - nk1 : s) * BK;
-      da.issue_kc(h ? g.a1 : g.a0, m0, k0, stg, wave, lane);
-      db.issue_kc(h ? g.b1 : g.b0, n0, k0, stg + OPB, wave, lane);
+      da.issue_kc(h ? g.a1 : g.a0, m0, (h ? s - nk1 : s) * BK, stg, wave, lane);
+    } else if constexpr (AL == KC) {
+      da.issue_kc(A, m0, s * BK, stg, wave, lane);
     } else {
-      const int k0 = s * BK;
-      if constexpr (AL == KC) da.issue_kc(A, m0, k0, stg, wave, lane);
-      else da.issue_mc(A, m0, A, m0 + 128, k0, stg, wave);
-      if constexpr (BL == KC) db.issue_kc(B, n0, k0, stg + OPB, wave, lane);
-      else if constexpr (KIND == GATEUP) db.issue_mc(g.b0, n0, g.b1, n0, k0, stg + OPB, wave);
-      else db.issue_mc(B, n0, B, n0 + 128, k0, stg + OPB, wave);
+      da.issue_mc(A, m0, A, m0 + 128, s * BK, stg, wave);
     }
+  };
+  auto issue_b = [&](int s, char* stg) {
+    if constexpr (KIND == DX) {
+      const bool h = s >= nk1;
+      db.issue_kc(h ? g.b1 : g.b0, n0, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
+    } else if constexpr (BL == KC) {
+      db.issue_kc(B, n0, s * BK, stg + OPB, wave, lane);
+    } else if constexpr (KIND == GATEUP) {
+      db.issue_mc(g.b0, n0, g.b1, n0, s * BK, stg + OPB, wave);
+    } else {
+      db.issue_mc(B, n0, B, n0 + 128, s * BK, stg + OPB, wave);
+    }
+  };
+  auto issue = [&](int s, char* stg) {
+    issue_a(s, stg);
+    issue_b(s, stg);
   };
 
   using F = RFrags<E, AL, BL>;
@@ -562,18 +574,22 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
     f0.read(st0, a_rows, b_rows, 0, lane);
   }
   // Steady state: four stages per trip with static ring slots, every stage
-  // issuing the loads of stage s + 3 (needs s + 6 < nk for the last one).
+  // issuing the loads of stage s + 3 (needs s + 6 < nk for the last one):
+  // its A tile during the first sub-step, its B tile during the second. At
+  // the wait, A and B of stage s + 2 and A of stage s + 3 may still be in
+  // flight.
   auto step = [&](int s, auto J) {
     constexpr int j = decltype(J)::value;
-    issue(s + 3, st[(j + 3) & 3]);
+    issue_a(s + 3, st[(j + 3) & 3]);
     f1.read(st[j], a_rows, b_rows, 1, lane);
     f0.mma(acc);
-    interleave<F::kReads, L>();
-    wait_vmcnt<2 * L>();
+    interleave<F::kReads, L / 2>();
+    wait_vmcnt<L + L / 2>();
     lds_barrier();
+    issue_b(s + 3, st[(j + 3) & 3]);
     f0.read(st[(j + 1) & 3], a_rows, b_rows, 0, lane);
     f1.mma(acc);
-    interleave<F::kReads, 0>();
+    interleave<F::kReads, L / 2>();
   };
   int s = 0;
   for (; s + 7 <= nk; s += 4) {
@@ -604,30 +620,190 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   ring_epilogue<E, KIND>(g, C, acc, m0, n0, wm, wn, lane, slot(wave));
 }
 
+// 64 values of K per stage with the operand tiles in a ring of five 32 KiB
+// LDS arrays: operand tile t (A of stage s is t = 2s, B is t = 2s + 1) lives
+// in array t % 5. While stage s is multiplied, its two arrays are busy, A of
+// stage s + 1 is already on its way, and the two arrays stage s - 1 used take
+// B of stage s + 1 and A of stage s + 2: every K-major row is still one whole
+// 128-byte line per request, and the loads of A run a stage and a half ahead.
+// Before the last sub-step of stage s this wave's loads up to B of stage s + 1
+// are waited for (vmcnt counts this wave's loads in issue order), then a
+// barrier publishes stage s + 1.
+template <class E, int AL, int BL, int KIND>
+__device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], int bid, int bz) {
+  using namespace ring;
+  constexpr int BK2 = 64;
+  static_assert(E::kBytes == 2, "the ring pipeline is for bf16/fp16");
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(bid, g.tiles_m, g.tiles_n, g.group_m > 0 ? g.group_m : 8, tm, tn);
+  const int m0 = tm * 256;
+  const int n0 = (KIND == GATEUP) ? tn * 128 : tn * 256;
+  Operand A = g.a0, B = g.b0;
+  char* C = g.c0;
+  if (KIND == PLAIN && bz == 1) {
+    B = g.b1;
+    C = g.c1;
+  }
+  int a_rows[4], b_rows[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_rows[i] = wm * 128 + i * 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b_rows[j] = (KIND == GATEUP) ? (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  Dma<AL, BK2> da;
+  Dma<BL, BK2> db;
+  da.init(A, m0, wave, lane);
+  db.init(B, n0, wave, lane);
+  const int nk1 = (A.k + BK2 - 1) / BK2;
+  const int nk = (KIND == DX) ? 2 * nk1 : nk1;
+  constexpr int NT = Geo<BK2>::PPW;  // loads per wave per operand tile
+
+  // pieces [j0, j1) of this wave's share of A of stage s
+  auto issue_a = [&](int s, char* t, int j0 = 0, int j1 = NT) {
+    if constexpr (KIND == DX) {
+      const bool h = s >= nk1;
+      da.issue_kc(h ? g.a1 : g.a0, m0, (h ? s - nk1 : s) * BK2, t, wave, lane, j0, j1);
+    } else if constexpr (AL == KC) {
+      da.issue_kc(A, m0, s * BK2, t, wave, lane, j0, j1);
+    } else {
+      da.issue_mc(A, m0, A, m0 + 128, s * BK2, t, wave, j0, j1);
+    }
+  };
+  auto issue_b = [&](int s, char* t) {
+    if constexpr (KIND == DX) {
+      const bool h = s >= nk1;
+      db.issue_kc(h ? g.b1 : g.b0, n0, (h ? s - nk1 : s) * BK2, t, wave, lane);
+    } else if constexpr (BL == KC) {
+      db.issue_kc(B, n0, s * BK2, t, wave, lane);
+    } else if constexpr (KIND == GATEUP) {
+      db.issue_mc(g.b0, n0, g.b1, n0, s * BK2, t, wave);
+    } else {
+      db.issue_mc(B, n0, B, n0 + 128, s * BK2, t, wave);
+    }
+  };
+
+  using F = RFrags<E, AL, BL, BK2>;
+  F f0, f1;
+  if (nk > 0) {
+    issue_a(0, R[0]);
+    issue_b(0, R[1]);
+    if (nk > 1) {
+      issue_a(1, R[2]);
+      wait_vmcnt<NT>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    f0.read(R[0], R[1], a_rows, b_rows, 0, lane);
+  }
+  // One stage. `full`: stages s + 1 and s + 2 exist (known at compile time in
+  // the unrolled loop); otherwise the tail checks at run time.
+  // The loads are spread over the sub-steps: B of stage s + 1 (needed first)
+  // over the first, A of stage s + 2 over the second and third.
+  auto stage = [&](int s, char* ca, char* cb, char* na, char* nb, char* na2, bool full) {
+    const bool more = full || s + 1 < nk;
+    const bool more2 = full || s + 2 < nk;
+    if (more) issue_b(s + 1, nb);
+    f1.read(ca, cb, a_rows, b_rows, 1, lane);
+    f0.mma(acc);
+    interleave<F::kReads, NT>();
+    if (more2) issue_a(s + 2, na2, 0, NT / 2);
+    f0.read(ca, cb, a_rows, b_rows, 2, lane);
+    f1.mma(acc);
+    interleave<F::kReads, NT / 2>();
+    if (more2) issue_a(s + 2, na2, NT / 2, NT);
+    f1.read(ca, cb, a_rows, b_rows, 3, lane);
+    f0.mma(acc);
+    interleave<F::kReads, NT / 2>();
+    if (more2) wait_vmcnt<NT>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (more) f0.read(na, nb, a_rows, b_rows, 0, lane);
+    f1.mma(acc);
+    interleave<F::kReads, 0>();
+  };
+  int s = 0;
+  for (; s + 7 <= nk; s += 5) {
+    stage(s + 0, R[0], R[1], R[2], R[3], R[4], true);
+    stage(s + 1, R[2], R[3], R[4], R[0], R[1], true);
+    stage(s + 2, R[4], R[0], R[1], R[2], R[3], true);
+    stage(s + 3, R[1], R[2], R[3], R[4], R[0], true);
+    stage(s + 4, R[3], R[4], R[0], R[1], R[2], true);
+  }
+  auto reg = [&](int t) -> char* {
+    t %= 5;
+    return t == 0 ? R[0] : t == 1 ? R[1] : t == 2 ? R[2] : t == 3 ? R[3] : R[4];
+  };
+  for (; s < nk; ++s) stage(s, reg(2 * s), reg(2 * s + 1), reg(2 * s + 2), reg(2 * s + 3), reg(2 * s + 4), false);
+  // (a select, not R[wave]: indexing R at run time would keep it in scratch)
+  ring_epilogue<E, KIND>(g, C, acc, m0, n0, wm, wn, lane, reg(wave));
+}
+
+// Pipeline per operand layouts: 4 = four stages of 32 K (ring_tile), 5 =
+// five-array ring of 64 K stages (ring5_tile). Measured at D = 4096,
+// H = 11008, T = 65536 (bf16): the 64 K stages help where both operands are
+// K-major and cost a few percent where one is M/N-major.
+#ifndef SWIGLU_RING_KK
+#define SWIGLU_RING_KK 5
+#endif
+#ifndef SWIGLU_RING_KM
+#define SWIGLU_RING_KM 4
+#endif
+#ifndef SWIGLU_RING_MM
+#define SWIGLU_RING_MM 4
+#endif
+template <int AL, int BL>
+constexpr int ring_variant() {
+  return (AL == KC && BL == KC) ? SWIGLU_RING_KK : (AL == KC || BL == KC) ? SWIGLU_RING_KM : SWIGLU_RING_MM;
+}
+
+template <class E, int AL, int BL, int KIND>
+__device__ __forceinline__ void any_ring_tile(const KArgs& g, char* const (&R)[5], int bid, int bz) {
+  if constexpr (ring_variant<AL, BL>() == 5) ring5_tile<E, AL, BL, KIND>(g, R, bid, bz);
+  else ring_tile<E, AL, BL, KIND>(g, R[0], R[1], R[2], R[3], bid, bz);
+}
+
+// Four 32 KiB LDS arrays, and a fifth when a five-array ring runs.
+#define SWIGLU_RING_LDS(NEED5)                                                        \
+  __shared__ __attribute__((aligned(16))) char s0[ring::STAGE];                       \
+  __shared__ __attribute__((aligned(16))) char s1[ring::STAGE];                       \
+  __shared__ __attribute__((aligned(16))) char s2[ring::STAGE];                       \
+  __shared__ __attribute__((aligned(16))) char s3[ring::STAGE];                       \
+  __shared__ __attribute__((aligned(16))) char s4[(NEED5) ? ring::STAGE : 16];        \
+  char* R[5];                                                                         \
+  R[0] = s0;                                                                          \
+  R[1] = s1;                                                                          \
+  R[2] = s2;                                                                          \
+  R[3] = s3;                                                                          \
+  R[4] = s4;
+
 template <class E, int AL, int BL, int KIND, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ring_gemm(const KArgs g) {
-  __shared__ __attribute__((aligned(16))) char s0[ring::STAGE];
-  __shared__ __attribute__((aligned(16))) char s1[ring::STAGE];
-  __shared__ __attribute__((aligned(16))) char s2[ring::STAGE];
-  __shared__ __attribute__((aligned(16))) char s3[ring::STAGE];
-  ring_tile<E, AL, BL, KIND>(g, s0, s1, s2, s3, blockIdx.x, blockIdx.z);
+  SWIGLU_RING_LDS((ring_variant<AL, BL>() == 5))
+  any_ring_tile<E, AL, BL, KIND>(g, R, blockIdx.x, blockIdx.z);
 }
 
 template <class E, int AL1, int BL1, int KIND1, int AL2, int BL2, int KIND2, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ring_gemm_pair(const KArgs g1, const KArgs g2) {
-  __shared__ __attribute__((aligned(16))) char s0[ring::STAGE];
-  __shared__ __attribute__((aligned(16))) char s1[ring::STAGE];
-  __shared__ __attribute__((aligned(16))) char s2[ring::STAGE];
-  __shared__ __attribute__((aligned(16))) char s3[ring::STAGE];
+  SWIGLU_RING_LDS((ring_variant<AL1, BL1>() == 5 || ring_variant<AL2, BL2>() == 5))
   const int nt1 = g1.tiles_m * g1.tiles_n;
   const int n1 = nt1 * g1.planes;
   const int b = blockIdx.x;
   if (b < n1)
-    ring_tile<E, AL1, BL1, KIND1>(g1, s0, s1, s2, s3, b % nt1, b / nt1);
+    any_ring_tile<E, AL1, BL1, KIND1>(g1, R, b % nt1, b / nt1);
   else
-    ring_tile<E, AL2, BL2, KIND2>(g2, s0, s1, s2, s3, b - n1, 0);
+    any_ring_tile<E, AL2, BL2, KIND2>(g2, R, b - n1, 0);
 }
 
 
@@ -840,8 +1016,15 @@ static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
+// Tile walk of the ring kernels: each XCD runs 2 M-tiles x 16 N-tiles at a
+// time, so that many concurrent tiles share the rows of the large T-indexed
+// operand (measured best of 1, 2, 4, 8, 16 at D = 4096, H = 11008,
+// T = 65536).
+constexpr int kRingGroupM = 2;
+
 template <class E, int AL, int BL, int KIND, int STAGE>
 static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
+  a.group_m = kRingGroupM;
   const int nb = a.tiles_m * a.tiles_n;
   a.planes = grid_z;
   if (nb <= 0) return SWIGLU_OK;
@@ -852,6 +1035,7 @@ static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
 
 template <class E, int AL1, int BL1, int K1, int AL2, int BL2, int K2, int STAGE>
 static int launch_ring_pair(KArgs a1, KArgs a2, hipStream_t stream) {
+  a1.group_m = a2.group_m = kRingGroupM;
   const int nb = a1.tiles_m * a1.tiles_n * a1.planes + a2.tiles_m * a2.tiles_n;
   if (nb <= 0) return SWIGLU_OK;
   StageScope scope(STAGE, stream);
