@@ -7,9 +7,10 @@ is missing or the device is not gfx950, calls raise.
 
 Three levels, following the maintainers' layering on "[RFC] Full-pipeline
 SwiGLU MLP with forward/backward co-optimization" (Liger-Kernel issue #1347,
-discussion thread): op-level wrappers (fwd / bwd / infer), an autograd
-Function composing them, and the ``swiglu_mlp`` convenience entry that
-flattens [..., D] inputs and picks the no-grad path when autograd is off.
+discussion thread): op-level wrappers (fwd / bwd / infer, and the
+``swiglu_mlp`` entry that flattens [..., D] inputs and picks the no-grad path
+when autograd is off), an autograd Function composing them, and the
+``SwiGLUMLP`` nn.Module.
 """
 
 import ctypes
@@ -19,7 +20,7 @@ import torch
 from . import _lib as _L
 from ._lib import SwiGLUError, STAGE_NAMES, NUM_STAGES  # noqa: F401
 
-__all__ = ["fwd", "bwd", "infer", "SwiGLUMLPFunction", "swiglu_mlp", "saved_bytes",
+__all__ = ["fwd", "bwd", "infer", "SwiGLUMLPFunction", "swiglu_mlp", "SwiGLUMLP", "saved_bytes",
            "infer_workspace_bytes", "SwiGLUError", "StageTimer"]
 
 _DT = {torch.bfloat16: _L.BF16, torch.float16: _L.FP16, torch.float32: _L.FP32}
@@ -60,6 +61,19 @@ def _shapes(x, wg, wu, wd):
     return T, D, wg.shape[1]
 
 
+def _buf(t, shape, like, name):
+    """A caller-provided output or workspace: allocate it if None, else check
+    that it is a contiguous tensor of the given shape on the inputs' device
+    and dtype (a host tensor here would hand a host pointer to the kernels)."""
+    if t is None:
+        return torch.empty(shape, dtype=like.dtype, device=like.device)
+    if t.device != like.device or t.dtype != like.dtype:
+        raise ValueError(f"{name} must be a {like.dtype} tensor on {like.device}")
+    if not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(shape)}")
+    return t
+
+
 def saved_bytes(T, H, dtype=torch.bfloat16):
     return _L.lib().swiglu_mlp_saved_bytes(T, H, _DT[dtype])
 
@@ -68,18 +82,22 @@ def infer_workspace_bytes(T, D, H, dtype=torch.bfloat16):
     return _L.lib().swiglu_mlp_infer_workspace_bytes(T, D, H, _DT[dtype])
 
 
-def fwd(x, wg, wu, wd, y=None, saved=None):
+def _flags(two_round):
+    return _L.FLAG_TWO_ROUND if two_round else 0
+
+
+def fwd(x, wg, wu, wd, y=None, saved=None, two_round=False):
     """Training forward. Returns (Y[T,D], saved) where ``saved`` is the
-    [3, T, H] A|G|U buffer that ``bwd`` consumes."""
+    [3, T, H] A|G|U buffer that ``bwd`` consumes. ``two_round`` selects the
+    historical two-round SwiGLU program A = rnd(rnd(SiLU(g)) u) instead of
+    the one-round A = rnd(SiLU(g) u)."""
     x, wg, wu, wd = (t.contiguous() for t in (x, wg, wu, wd))
     T, D, H = _shapes(x, wg, wu, wd)
-    if y is None:
-        y = torch.empty((T, D), dtype=x.dtype, device=x.device)
-    if saved is None:
-        saved = torch.empty((3, T, H), dtype=x.dtype, device=x.device)
-    rc = _L.lib().swiglu_mlp_fwd(_p(x), _p(wg), _p(wu), _p(wd), _p(y), _p(saved),
-                                 T, D, H, _dt(x), _stream(x.device))
-    _check(rc, "swiglu_mlp_fwd")
+    y = _buf(y, (T, D), x, "y")
+    saved = _buf(saved, (3, T, H), x, "saved")
+    rc = _L.lib().swiglu_mlp_fwd_ex(_p(x), _p(wg), _p(wu), _p(wd), _p(y), _p(saved),
+                                    T, D, H, _dt(x), _flags(two_round), _stream(x.device))
+    _check(rc, "swiglu_mlp_fwd_ex")
     return y, saved
 
 
@@ -88,12 +106,13 @@ def bwd(dy, x, wg, wu, wd, saved, dx=None, dwg=None, dwu=None, dwd=None):
     Returns (dX, dWg, dWu, dWd)."""
     dy, x, wg, wu, wd = (t.contiguous() for t in (dy, x, wg, wu, wd))
     T, D, H = _shapes(x, wg, wu, wd)
-    if tuple(dy.shape) != (T, D) or dy.dtype != x.dtype:
-        raise ValueError("dY must match X in shape and dtype")
-    if not saved.is_contiguous() or saved.numel() != 3 * T * H or saved.dtype != x.dtype:
+    if tuple(dy.shape) != (T, D) or dy.dtype != x.dtype or dy.device != x.device:
+        raise ValueError("dY must match X in shape, dtype and device")
+    if (not saved.is_contiguous() or saved.numel() != 3 * T * H or saved.dtype != x.dtype
+            or saved.device != x.device):
         raise ValueError("saved must be the contiguous [3, T, H] buffer returned by fwd")
-    mk = lambda t, shape: torch.empty(shape, dtype=x.dtype, device=x.device) if t is None else t
-    dx, dwg, dwu, dwd = mk(dx, (T, D)), mk(dwg, (D, H)), mk(dwu, (D, H)), mk(dwd, (H, D))
+    dx, dwg, dwu, dwd = (_buf(dx, (T, D), x, "dx"), _buf(dwg, (D, H), x, "dwg"),
+                         _buf(dwu, (D, H), x, "dwu"), _buf(dwd, (H, D), x, "dwd"))
     rc = _L.lib().swiglu_mlp_bwd(_p(dy), _p(x), _p(wg), _p(wu), _p(wd), _p(saved),
                                  _p(dx), _p(dwg), _p(dwu), _p(dwd), None, 0,
                                  T, D, H, _dt(x), _stream(x.device))
@@ -101,18 +120,19 @@ def bwd(dy, x, wg, wu, wd, saved, dx=None, dwg=None, dwu=None, dwd=None):
     return dx, dwg, dwu, dwd
 
 
-def infer(x, wg, wu, wd, y=None, workspace=None):
+def infer(x, wg, wu, wd, y=None, workspace=None, two_round=False):
     """No-grad forward: only A[T,H] (the workspace) and Y[T,D] are written."""
     x, wg, wu, wd = (t.contiguous() for t in (x, wg, wu, wd))
     T, D, H = _shapes(x, wg, wu, wd)
-    if y is None:
-        y = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    y = _buf(y, (T, D), x, "y")
     if workspace is None:
         workspace = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    elif workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {x.device}")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = _L.lib().swiglu_mlp_infer(_p(x), _p(wg), _p(wu), _p(wd), _p(y), _p(workspace), nbytes,
-                                   T, D, H, _dt(x), _stream(x.device))
-    _check(rc, "swiglu_mlp_infer")
+    rc = _L.lib().swiglu_mlp_infer_ex(_p(x), _p(wg), _p(wu), _p(wd), _p(y), _p(workspace), nbytes,
+                                      T, D, H, _dt(x), _flags(two_round), _stream(x.device))
+    _check(rc, "swiglu_mlp_infer_ex")
     return y
 
 
@@ -123,8 +143,8 @@ class SwiGLUMLPFunction(torch.autograd.Function):
     (issue #1347, section "Known limitations and validation gaps")."""
 
     @staticmethod
-    def forward(ctx, x, wg, wu, wd):
-        y, saved = fwd(x, wg, wu, wd)
+    def forward(ctx, x, wg, wu, wd, two_round=False):
+        y, saved = fwd(x, wg, wu, wd, two_round=two_round)
         ctx.save_for_backward(x, wg, wu, wd)
         ctx.saved_buf = saved
         return y
@@ -139,17 +159,80 @@ class SwiGLUMLPFunction(torch.autograd.Function):
         x, wg, wu, wd = ctx.saved_tensors
         saved, ctx.saved_buf = ctx.saved_buf, None
         dx, dwg, dwu, dwd = bwd(dy, x, wg, wu, wd, saved)
-        return dx, dwg, dwu, dwd
+        return dx, dwg, dwu, dwd, None
 
 
-def swiglu_mlp(x, wg, wu, wd):
+def swiglu_mlp(x, wg, wu, wd, two_round=False):
     """Y = (SiLU(x Wg) * (x Wu)) Wd for x[..., D]. Uses the no-grad path when
     autograd does not need gradients."""
     lead = x.shape[:-1]
     x2 = x.reshape(-1, x.shape[-1])
     needs = torch.is_grad_enabled() and any(t.requires_grad for t in (x, wg, wu, wd))
-    y = SwiGLUMLPFunction.apply(x2, wg, wu, wd) if needs else infer(x2, wg, wu, wd)
+    if needs:
+        y = SwiGLUMLPFunction.apply(x2, wg, wu, wd, two_round)
+    else:
+        y = infer(x2, wg, wu, wd, two_round=two_round)
     return y.reshape(*lead, wd.shape[1])
+
+
+class SwiGLUMLP(torch.nn.Module):
+    """nn.Module drop-in for a SwiGLU MLP block: y = (SiLU(x Wg) * (x Wu)) Wd on
+    x[..., D] (for example [B, S, D]), standard SwiGLU only (no bias, no gate
+    or down multipliers), bf16/fp16/fp32 parameters on a gfx950 GPU.
+
+    The weights are kept in the kernels' layout: ``w_gate``, ``w_up`` [D, H]
+    and ``w_down`` [H, D] (row-major), so no transposition happens per call.
+    ``from_linears`` converts the usual nn.Linear triple (weights [H, D] and
+    [D, H]) once. Training uses the fused forward/backward through
+    ``SwiGLUMLPFunction``; under ``torch.no_grad()`` (or when nothing needs a
+    gradient) the no-grad path runs and saves no G/U. ``two_round`` selects
+    the historical two-round SwiGLU epilogue."""
+
+    def __init__(self, hidden_size, intermediate_size, dtype=torch.bfloat16, device=None, generator=None,
+                 two_round=False):
+        super().__init__()
+        self.two_round = bool(two_round)
+        D, H = int(hidden_size), int(intermediate_size)
+        kw = {"dtype": torch.float32, "device": "cpu"}
+        # normal init with variance 1/fan_in keeps G, U and Y at the scale of x
+        wg = torch.randn(D, H, generator=generator, **kw) / D ** 0.5
+        wu = torch.randn(D, H, generator=generator, **kw) / D ** 0.5
+        wd = torch.randn(H, D, generator=generator, **kw) / H ** 0.5
+        mk = lambda t: torch.nn.Parameter(t.to(dtype=dtype, device=device))
+        self.w_gate, self.w_up, self.w_down = mk(wg), mk(wu), mk(wd)
+
+    @classmethod
+    def from_linears(cls, gate_proj, up_proj, down_proj, two_round=False):
+        """Build from nn.Linear layers (gate_proj, up_proj: D -> H; down_proj:
+        H -> D; no bias), copying their weights into the kernels' layout."""
+        for lin in (gate_proj, up_proj, down_proj):
+            if lin.bias is not None:
+                raise ValueError("SwiGLUMLP has no bias terms")
+        H, D = gate_proj.weight.shape
+        w = gate_proj.weight
+        m = cls.__new__(cls)
+        torch.nn.Module.__init__(m)
+        m.two_round = bool(two_round)
+        mk = lambda t: torch.nn.Parameter(t.detach().t().contiguous())
+        m.w_gate, m.w_up, m.w_down = mk(gate_proj.weight), mk(up_proj.weight), mk(down_proj.weight)
+        if tuple(m.w_down.shape) != (H, D) or m.w_up.shape != m.w_gate.shape or m.w_gate.dtype != w.dtype:
+            raise ValueError("gate_proj, up_proj must map D -> H and down_proj H -> D")
+        return m
+
+    @property
+    def hidden_size(self):
+        return self.w_gate.shape[0]
+
+    @property
+    def intermediate_size(self):
+        return self.w_gate.shape[1]
+
+    def forward(self, x):
+        return swiglu_mlp(x, self.w_gate, self.w_up, self.w_down, two_round=self.two_round)
+
+    def extra_repr(self):
+        r = f"hidden_size={self.hidden_size}, intermediate_size={self.intermediate_size}"
+        return r + (", two_round=True" if self.two_round else "")
 
 
 class StageTimer:

@@ -50,6 +50,7 @@ struct KArgs {
   int store_gu;    // GATEUP: write the G and U planes (training) or A only (no-grad)
   int planes;      // PLAIN: number of (B source, output) planes (1 or 2)
   int group_m;     // M-tiles per group of the tile walk (tile_coords); 0 = 8
+  int two_round;   // GATEUP: A = rnd(rnd(SiLU(g)) * u) instead of rnd(SiLU(g) * u)
 };
 
 // Logistic function sigma(g) = 1 / (1 + exp(-g)) in fp32, from a stored gate
@@ -73,6 +74,18 @@ template <class E>
 __device__ __forceinline__ float sigmoid_f32(float g) {
   if constexpr (E::kBytes == 4) return sigmoid_ieee(g);
   else return sigmoid_fast(g);
+}
+
+// A from the stored gate and up values g, u. One-round program: SiLU(g) * u
+// evaluated in fp32 and rounded once to the storage type ("Scope one-round
+// FP32 SwiGLU to the exact Qwen3.5 contract", review thread). Two-round
+// (historical) program of the same page: SiLU(g) rounded to the storage type
+// first, then the product rounded again. In fp32 storage the two coincide.
+template <class E>
+__device__ __forceinline__ typename E::elem swiglu_a(float gf, float uf, int two_round) {
+  const float silu = gf * sigmoid_f32<E>(gf);
+  if (two_round) return E::from_f32(E::to_f32(E::from_f32(silu)) * uf);
+  return E::from_f32(silu * uf);
 }
 
 // Epilogue of one tile. acc[i][j][r] holds output
@@ -106,7 +119,7 @@ __device__ __forceinline__ void epilogue(const KArgs& g, char* C, f32x16_t (&acc
             float gf = E::to_f32(gs), uf = E::to_f32(us);
             gv[e] = gs;
             uv[e] = us;
-            av[e] = E::from_f32(gf * sigmoid_f32<E>(gf) * uf);
+            av[e] = swiglu_a<E>(gf, uf, g.two_round);
           }
           const int64_t off = ((int64_t)m * g.ldc + n) * EB;
           *(V4*)(g.c0 + off) = av;
@@ -413,7 +426,7 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
             typename E::elem us = E::from_f32(acc[i][j + 2][q * 4 + e]);
             const float gf = E::to_f32(gs), uf = E::to_f32(us);
             gv[e] = gs;
-            av[e] = E::from_f32(gf * sigmoid_f32<E>(gf) * uf);
+            av[e] = swiglu_a<E>(gf, uf, g.two_round);
           }
           pa.put4(i * 32 + ml, j * 32 + q * 8 + nl, av);
           pg.put4(i * 32 + ml, j * 32 + q * 8 + nl, gv);
@@ -924,7 +937,7 @@ __device__ __forceinline__ void skinny_unit(const KArgs& g, char* lds, int unit)
         const float gf = E::to_f32(gs), uf = E::to_f32(us);
         gv[e] = gs;
         uv[e] = us;
-        av[e] = E::from_f32(gf * sigmoid_f32<E>(gf) * uf);
+        av[e] = swiglu_a<E>(gf, uf, g.two_round);
       }
       *(V4*)(g.c0 + off) = av;
       if (g.store_gu) {
@@ -1074,7 +1087,7 @@ struct Path {
 
   template <int STAGE>
   static int gateup(const void* X, const void* Wg, const void* Wu, char* Ap, char* Gp, char* Up,
-                    int64_t T, int64_t D, int64_t H, bool store_gu, hipStream_t s) {
+                    int64_t T, int64_t D, int64_t H, bool store_gu, bool two_round, hipStream_t s) {
     KArgs a{};
     a.a0 = opnd(X, D, T, D);
     a.b0 = opnd(Wg, H, H, D);
@@ -1086,6 +1099,7 @@ struct Path {
     a.M = (int)T;
     a.N = (int)H;
     a.store_gu = store_gu ? 1 : 0;
+    a.two_round = two_round ? 1 : 0;
     if constexpr (E::kBytes == 2)
       if (few_t(T)) return launch_skinny<E, GATEUP, STAGE>(a, T, H, s);
     if (small_t(T)) {
@@ -1282,10 +1296,10 @@ static int zero_fill(void* p, size_t bytes, hipStream_t s) {
 
 template <class E>
 static int run_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
-                   int64_t D, int64_t H, hipStream_t s) {
+                   int64_t D, int64_t H, bool two_round, hipStream_t s) {
   const size_t plane = (size_t)T * H * E::kBytes;
   char* Ap = (char*)saved;
-  int rc = Path<E>::template gateup<0>(X, Wg, Wu, Ap, Ap + plane, Ap + 2 * plane, T, D, H, true, s);
+  int rc = Path<E>::template gateup<0>(X, Wg, Wu, Ap, Ap + plane, Ap + 2 * plane, T, D, H, true, two_round, s);
   if (rc) return rc;
   return Path<E>::template down<1>(Ap, Wd, Y, T, D, H, s);
 }
@@ -1307,9 +1321,9 @@ static int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
 
 template <class E>
 static int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws, int64_t T,
-                     int64_t D, int64_t H, hipStream_t s) {
+                     int64_t D, int64_t H, bool two_round, hipStream_t s) {
   char* Ap = (char*)ws;
-  int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, s);
+  int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, s);
   if (rc) return rc;
   return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, s);
 }
@@ -1334,10 +1348,12 @@ size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dty
 
 size_t swiglu_mlp_bwd_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
 
-int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
-                   int64_t D, int64_t H, int dtype, hipStream_t stream) {
+int swiglu_mlp_fwd_ex(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
+                      int64_t D, int64_t H, int dtype, unsigned flags, hipStream_t stream) {
   size_t e = elt_bytes(dtype);
   if (!e) return SWIGLU_ERR_DTYPE;
+  if (flags & ~SWIGLU_FLAGS_ALL) return SWIGLU_ERR_FLAGS;
+  const bool two_round = (flags & SWIGLU_FLAG_TWO_ROUND) != 0;
   int rc = check_shape(T, D, H);
   if (rc) return rc;
   Range in[] = {{X, (size_t)T * D * e}, {Wg, (size_t)D * H * e}, {Wu, (size_t)D * H * e}, {Wd, (size_t)H * D * e}};
@@ -1350,10 +1366,15 @@ int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd
   if ((rc = check_device())) return rc;
   if (T == 0) return SWIGLU_OK;
   switch (dtype) {
-    case SWIGLU_BF16: return run_fwd<Bf16>(X, Wg, Wu, Wd, Y, saved, T, D, H, stream);
-    case SWIGLU_FP16: return run_fwd<Fp16>(X, Wg, Wu, Wd, Y, saved, T, D, H, stream);
-    default: return run_fwd<Fp32>(X, Wg, Wu, Wd, Y, saved, T, D, H, stream);
+    case SWIGLU_BF16: return run_fwd<Bf16>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
+    case SWIGLU_FP16: return run_fwd<Fp16>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
+    default: return run_fwd<Fp32>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
   }
+}
+
+int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
+                   int64_t D, int64_t H, int dtype, hipStream_t stream) {
+  return swiglu_mlp_fwd_ex(X, Wg, Wu, Wd, Y, saved, T, D, H, dtype, 0u, stream);
 }
 
 int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
@@ -1389,10 +1410,13 @@ int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
   }
 }
 
-int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* workspace,
-                     size_t workspace_bytes, int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream) {
+int swiglu_mlp_infer_ex(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* workspace,
+                        size_t workspace_bytes, int64_t T, int64_t D, int64_t H, int dtype, unsigned flags,
+                        hipStream_t stream) {
   size_t e = elt_bytes(dtype);
   if (!e) return SWIGLU_ERR_DTYPE;
+  if (flags & ~SWIGLU_FLAGS_ALL) return SWIGLU_ERR_FLAGS;
+  const bool two_round = (flags & SWIGLU_FLAG_TWO_ROUND) != 0;
   int rc = check_shape(T, D, H);
   if (rc) return rc;
   const size_t need = (size_t)T * H * e;
@@ -1409,10 +1433,15 @@ int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* 
   if ((rc = check_device())) return rc;
   if (T == 0) return SWIGLU_OK;
   switch (dtype) {
-    case SWIGLU_BF16: return run_infer<Bf16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, stream);
-    case SWIGLU_FP16: return run_infer<Fp16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, stream);
-    default: return run_infer<Fp32>(X, Wg, Wu, Wd, Y, workspace, T, D, H, stream);
+    case SWIGLU_BF16: return run_infer<Bf16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
+    case SWIGLU_FP16: return run_infer<Fp16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
+    default: return run_infer<Fp32>(X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
   }
+}
+
+int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* workspace,
+                     size_t workspace_bytes, int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream) {
+  return swiglu_mlp_infer_ex(X, Wg, Wu, Wd, Y, workspace, workspace_bytes, T, D, H, dtype, 0u, stream);
 }
 
 const char* swiglu_mlp_status_string(int status) {
@@ -1426,6 +1455,7 @@ const char* swiglu_mlp_status_string(int status) {
     case SWIGLU_ERR_WORKSPACE: return "workspace missing or too small";
     case SWIGLU_ERR_DEVICE: return "current device is not gfx950 (or a HIP device query failed)";
     case SWIGLU_ERR_LAUNCH: return "kernel launch failed";
+    case SWIGLU_ERR_FLAGS: return "unknown bits in flags";
     default: return "unknown status";
   }
 }

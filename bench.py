@@ -125,7 +125,11 @@ def infer_sweep(mlp, torch, dev, reps=20):
     """No-grad path at B=1, S in {1..256}, D/H in {1024/2816, 4096/11008}: device
     time per call (HIP events around the call only) with the 256 MB Infinity
     Cache flushed before every timed call (a 1 GiB fill outside the events), and
-    HBM GB/s from the call's algorithmic bytes 2*(3*D*H + 2*T*D + 2*T*H)."""
+    HBM GB/s from the call's algorithmic bytes 2*(3*D*H + 2*T*D + 2*T*H).
+    Also the host-inclusive wall time of one call (Python binding, argument
+    checks, two launches, completion), eagerly and as a replay of a HIP graph
+    that captured the same call (checked bitwise against the eager output),
+    and the intermediate bytes the call needs (A workspace + Y)."""
     from synth import INFER_DH, INFER_S, make_inputs
 
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -151,11 +155,72 @@ def infer_sweep(mlp, torch, dev, reps=20):
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
             med = us[len(us) // 2]
             nbytes = 2 * (3 * D * H + 2 * S * D + 2 * S * H)
+
+            def wall(call):
+                ts = []
+                for _ in range(reps):
+                    flush.fill_(1)
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    call()
+                    torch.cuda.synchronize()
+                    ts.append((time.perf_counter() - t0) * 1e6)
+                return sorted(ts)[len(ts) // 2]
+
+            eager_us = wall(lambda: mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws))
+            y_eager = y.clone()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+            y.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            same = bool(torch.equal(y, y_eager))
+            graph_us = wall(graph.replay)
+            del graph
             rows[str(S)] = {"us": round(med, 2), "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                            "frac_hbm": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
+                            "frac_hbm": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
+                            "wall_us_eager": round(eager_us, 1), "wall_us_graph": round(graph_us, 1),
+                            "graph_bitwise_equal": same,
+                            "intermediate_MiB": round(2 * (S * H + S * D) / 2**20, 3)}
         out[f"{D}x{H}"] = rows
     del flush
     return out
+
+
+def fp32_leg(mlp, torch, dev, steps=10, warmup=3):
+    """True-IEEE fp32 mode at D=2048, H=5632, B=8, S=512 (T=4096): mean step time
+    of fwd + bwd and TFLOP/s (18*T*D*H) against the fp32 matrix peak."""
+    from synth import WORKLOADS, workload_inputs
+
+    name = "mlp_2048x5632_T4096_fp32"
+    D, H, B, S, _ = WORKLOADS[name]
+    T = B * S
+    g = {k: v.to(dev) for k, v in workload_inputs(name, dtype="fp32").items()}
+    f32 = torch.float32
+    y = torch.empty((T, D), dtype=f32, device=dev)
+    saved = torch.empty((3, T, H), dtype=f32, device=dev)
+    dx = torch.empty((T, D), dtype=f32, device=dev)
+    dwg, dwu = (torch.empty((D, H), dtype=f32, device=dev) for _ in range(2))
+    dwd = torch.empty((H, D), dtype=f32, device=dev)
+
+    def step():
+        mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"], y=y, saved=saved)
+        mlp.bwd(g["dY"], g["X"], g["Wg"], g["Wu"], g["Wd"], saved, dx=dx, dwg=dwg, dwu=dwu, dwd=dwd)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    tf = 18.0 * T * D * H / (ms * 1e-3) / 1e12
+    return {"config": {"D": D, "H": H, "B": B, "S": S, "T": T}, "dtype": "f32", "ms_per_step": round(ms, 3),
+            "tflops": round(tf, 2), "peak_tflops": PEAK_FP32_TFLOPS, "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4)}
 
 
 def ingest_traffic(fetch_csv, write_csv, copy_mib, command):
@@ -217,6 +282,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-infer", action="store_true", help="skip the no-grad (inference) sweep")
+    ap.add_argument("--no-fp32", action="store_true", help="skip the true-IEEE fp32 run")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known traffic, used to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -264,15 +330,17 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events between steps: the whole loop gives the mean, each step its own time
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with mlp.StageTimer(capacity=max(args.steps, 1)) as st:
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
+        ev[0].record()
+        for i in range(args.steps):
             step()
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     flops = 18.0 * T * D * H
     tflops = flops / (ms_step * 1e-3) / 1e12
 
@@ -311,10 +379,14 @@ def main():
         "config": {"workload": "swiglu_mlp_fwd_bwd", "D": D, "H": H, "B": B, "S": S, "T": T,
                    "parallelism": "single-gpu"},
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "step_ms": {"mean": round(ms_step, 3), "median": round(per_step[len(per_step) // 2], 3),
+                    "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
         "roofline": roofline,
         "stages": stages,
     }
     del g, X, Wg, Wu, Wd, dY, y, saved, dx, dwg, dwu, dwd
+    if not args.no_fp32:
+        out["fp32_ieee"] = fp32_leg(mlp, torch, dev)
     if not args.no_infer:
         out["infer"] = {"metric": "no-grad HBM GB/s (B=1, 256 MB cache flushed per call)",
                         "peak_GBps": PEAK_HBM_GBS, "by_shape": infer_sweep(mlp, torch, dev)}

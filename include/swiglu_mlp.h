@@ -21,7 +21,8 @@
  * rounded once (round to nearest even) from fp32. The SwiGLU epilogue is the
  * one-round program of "Scope one-round FP32 SwiGLU to the exact Qwen3.5
  * contract" (xorl PR #51, review thread): A = rnd(SiLU(g) * u), evaluated in
- * fp32 from the stored (rounded) g and u. SWIGLU_FP32 is true IEEE fp32:
+ * fp32 from the stored (rounded) g and u (the _ex entry points can select
+ * the historical two-round program instead). SWIGLU_FP32 is true IEEE fp32:
  * fp32 operands enter the matrix cores unrounded (the TF32 issue described
  * in "[RFC] Testing Methodology for FP32 Convergence Tests on Fused
  * SwiGLU/dSwiGLU Kernels", Liger-Kernel issue #1383, section "Root Cause").
@@ -69,8 +70,21 @@ typedef enum {
   SWIGLU_ERR_ALIAS = 5,     /* an output overlaps an input or another output */
   SWIGLU_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required */
   SWIGLU_ERR_DEVICE = 7,    /* current device is not gfx950, or a HIP query failed */
-  SWIGLU_ERR_LAUNCH = 8     /* a kernel launch failed (work may be partially enqueued) */
+  SWIGLU_ERR_LAUNCH = 8,    /* a kernel launch failed (work may be partially enqueued) */
+  SWIGLU_ERR_FLAGS = 9      /* unknown bits in the flags of an _ex entry point */
 } swiglu_status_t;
+
+/* Flags of swiglu_mlp_fwd_ex / swiglu_mlp_infer_ex.
+ * SWIGLU_FLAG_TWO_ROUND selects the historical two-round SwiGLU program of
+ * "Scope one-round FP32 SwiGLU to the exact Qwen3.5 contract" (xorl PR #51,
+ * review thread): A = rnd(rnd(SiLU(g)) * u), SiLU(g) rounded to the storage
+ * dtype before the product. This gives byte compatibility with unfused
+ * pipelines that store SiLU(g) first. The page reports that about 27% of
+ * bf16 outputs differ from the one-round program. Only A changes: G, U and
+ * the backward are as without the flag, and the backward's dWd uses the A it
+ * finds in the saved buffer. In SWIGLU_FP32 the two programs coincide. */
+#define SWIGLU_FLAG_TWO_ROUND 1u
+#define SWIGLU_FLAGS_ALL 1u
 
 /* Bytes of the saved A|G|U buffer: 3 * T * H * sizeof(dtype). 0 on bad args. */
 size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
@@ -91,6 +105,12 @@ int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd
                    void* Y, void* saved, int64_t T, int64_t D, int64_t H,
                    int dtype, hipStream_t stream);
 
+/* swiglu_mlp_fwd with epilogue flags (SWIGLU_FLAG_*); flags = 0 is
+ * swiglu_mlp_fwd. Unknown bits: SWIGLU_ERR_FLAGS, nothing launched. */
+int swiglu_mlp_fwd_ex(const void* X, const void* Wg, const void* Wu, const void* Wd,
+                      void* Y, void* saved, int64_t T, int64_t D, int64_t H,
+                      int dtype, unsigned flags, hipStream_t stream);
+
 /* Full backward. Reads dY, X, Wg, Wu, Wd and the saved buffer written by
  * swiglu_mlp_fwd with the same inputs; writes dX [T, D] (the page's dI),
  * dWg, dWu [D, H], dWd [H, D]. Consumes the saved buffer: its G and U planes
@@ -108,6 +128,13 @@ int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
 int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd,
                      void* Y, void* workspace, size_t workspace_bytes,
                      int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream);
+
+/* swiglu_mlp_infer with epilogue flags (SWIGLU_FLAG_*); flags = 0 is
+ * swiglu_mlp_infer. Unknown bits: SWIGLU_ERR_FLAGS, nothing launched. */
+int swiglu_mlp_infer_ex(const void* X, const void* Wg, const void* Wu, const void* Wd,
+                        void* Y, void* workspace, size_t workspace_bytes,
+                        int64_t T, int64_t D, int64_t H, int dtype, unsigned flags,
+                        hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* swiglu_mlp_status_string(int status);

@@ -61,7 +61,7 @@ def test_infer_memory_matches_pages_table():
 
 def test_status_strings():
     L = _lib()
-    for s in range(9):
+    for s in range(10):
         assert len(L.swiglu_mlp_status_string(s)) > 0
     assert L.swiglu_mlp_status_string(99) == b"unknown status"
 
@@ -111,3 +111,15 @@ def test_no_device_is_reported_not_crashed():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _fwd(_lib()) == 7
+
+
+def test_unknown_flags_rejected_before_anything_else():
+    L = _lib()
+    b = [BASE + (i << 30) for i in range(7)]
+    for bad in (2, 4, 0x80000000):
+        assert L.swiglu_mlp_fwd_ex(*b[:6], 16, 64, 128, 0, bad, None) == 9
+        assert L.swiglu_mlp_infer_ex(*b[:6], 16 * 128 * 2, 16, 64, 128, 0, bad, None) == 9
+    # a bad dtype is reported first; known flags pass to the remaining checks
+    assert L.swiglu_mlp_fwd_ex(*b[:6], 16, 64, 128, 7, 2, None) == 3
+    assert L.swiglu_mlp_fwd_ex(b[0], b[1], b[2], b[3], b[0] + 64, b[5], 16, 64, 128, 0, 1, None) == 5
+    assert L.swiglu_mlp_infer_ex(*b[:5], None, 0, 16, 64, 128, 0, 1, None) == 6

@@ -1,0 +1,92 @@
+"""The C ABI under HIP-graph capture (GPU).
+
+The no-grad call and a full training step (forward + backward) are captured
+once through torch.cuda.graph on the current stream. Each graph is then
+replayed several times, with unrelated eager work and synchronizations in
+between. Every replay must reproduce the eager outputs bit for bit: the path
+is deterministic (no atomics, fixed tile order), and it records no memset
+nodes. The pages name small-shape host overhead as the no-grad path's only
+loss ("[RFC] Full-pipeline SwiGLU MLP with forward/backward co-optimization",
+"Inference results"), and replaying a graph is how a caller removes it.
+"""
+
+import pytest
+import torch
+
+from synth import make_inputs
+from tests._util import banner, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mlp():
+    import backward_gate_up_amd as m
+
+    return m
+
+
+def _noise():
+    # unrelated eager work between replays (allocations, kernels, a reduction)
+    a = torch.randn(1 << 20, device="cuda")
+    return float(a.square().sum())
+
+
+@pytest.mark.parametrize("D,H", [(1024, 2816), (256, 384)])
+@pytest.mark.parametrize("S", [1, 16, 64, 200])
+def test_infer_graph_replay(mlp, S, D, H):
+    banner(f"graph infer S={S} D={D} H={H}")
+    g = to_dev(make_inputs(S, D, H, seed=31 + S, dtype="bf16", with_dy=False))
+    y = torch.empty((S, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((S, H), dtype=torch.bfloat16, device="cuda")
+    mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], y=y, workspace=ws)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], y=y, workspace=ws)
+    for r in range(4):
+        y.fill_(float("nan"))
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {r}"
+    # new inputs written into the captured buffers flow through the graph
+    g["X"].copy_(make_inputs(S, D, H, seed=99, dtype="bf16", with_dy=False)["X"].cuda())
+    graph.replay()
+    mlp_eager = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, mlp_eager)
+
+
+@pytest.mark.parametrize("T,D,H", [(300, 256, 384), (1024, 512, 1024)])
+def test_train_step_graph_replay(mlp, T, D, H):
+    banner(f"graph train T={T} D={D} H={H}")
+    g = to_dev(make_inputs(T, D, H, seed=7 + T, dtype="bf16"))
+    bf = torch.bfloat16
+    y = torch.empty((T, D), dtype=bf, device="cuda")
+    saved = torch.empty((3, T, H), dtype=bf, device="cuda")
+    dx = torch.empty((T, D), dtype=bf, device="cuda")
+    dwg = torch.empty((D, H), dtype=bf, device="cuda")
+    dwu = torch.empty((D, H), dtype=bf, device="cuda")
+    dwd = torch.empty((H, D), dtype=bf, device="cuda")
+    outs = (y, dx, dwg, dwu, dwd)
+
+    def step():
+        mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"], y=y, saved=saved)
+        mlp.bwd(g["dY"], g["X"], g["Wg"], g["Wu"], g["Wd"], saved, dx=dx, dwg=dwg, dwu=dwu, dwd=dwd)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("Y", "dI", "dWg", "dWu", "dWd"), outs, ref):
+            assert torch.equal(got, want), f"replay {r}: {name}"

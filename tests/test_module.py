@@ -1,0 +1,71 @@
+"""The autograd Function and nn.Module levels against the fp64 oracle (GPU).
+
+A [B, S, D] input goes through ``SwiGLUMLP`` with autograd; the upstream
+gradient dY enters through loss = <Y, dY>, so the gradients autograd returns
+are the oracle's bwd(dY, ...) at the normalized-L2 bound of 1e-2 (bf16). The
+same module under torch.no_grad() takes the no-grad path and returns the
+training Y bit for bit. The autograd Function is single use ("[RFC]
+Full-pipeline SwiGLU MLP with forward/backward co-optimization", "Known
+limitations and validation gaps"): a second backward and double backward are
+refused.
+"""
+
+import pytest
+import torch
+
+import oracle as O
+from synth import make_inputs
+from tests._util import TOL, banner, f64, nl2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mlp():
+    import backward_gate_up_amd as m
+
+    return m
+
+
+@pytest.mark.parametrize("B,S,D,H,dt", [(2, 150, 256, 384, torch.bfloat16), (4, 700, 512, 1376, torch.bfloat16),
+                                        (1, 333, 136, 264, torch.float16)])
+def test_module_grads_vs_oracle(mlp, B, S, D, H, dt):
+    fmt = {torch.bfloat16: "bf16", torch.float16: "fp16"}[dt]
+    banner(f"module B={B} S={S} D={D} H={H} {fmt}")
+    inp = make_inputs(B * S, D, H, seed=B * 1000 + S, dtype=fmt)
+    mod = mlp.SwiGLUMLP(D, H, dtype=dt, device="cuda")
+    with torch.no_grad():
+        mod.w_gate.copy_(inp["Wg"])
+        mod.w_up.copy_(inp["Wu"])
+        mod.w_down.copy_(inp["Wd"])
+    x = inp["X"].view(B, S, D).cuda().requires_grad_(True)
+    dy = inp["dY"].view(B, S, D).cuda()
+    y = mod(x)
+    assert y.shape == (B, S, D) and y.dtype == dt
+    (y.float() * dy.float()).sum().backward()
+    f = {k: v.float().numpy() for k, v in inp.items()}
+    ref = O.bwd(f["dY"], f["X"], f["Wg"], f["Wu"], f["Wd"])
+    errs = {"Y": nl2(f64(y.reshape(B * S, D)), O.fwd(f["X"], f["Wg"], f["Wu"], f["Wd"])["Y"]),
+            "dI": nl2(f64(x.grad.reshape(B * S, D)), ref["dI"]),
+            "dWg": nl2(f64(mod.w_gate.grad), ref["dWg"]), "dWu": nl2(f64(mod.w_up.grad), ref["dWu"]),
+            "dWd": nl2(f64(mod.w_down.grad), ref["dWd"])}
+    banner(" ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[fmt], (k, v)
+    with torch.no_grad():
+        y_ng = mod(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ng, y.detach())
+
+
+def test_function_single_use(mlp):
+    inp = make_inputs(64, 128, 256, seed=3, dtype="bf16")
+    x = inp["X"].cuda().requires_grad_(True)
+    w = [inp[k].cuda().requires_grad_(True) for k in ("Wg", "Wu", "Wd")]
+    y = mlp.swiglu_mlp(x, *w)
+    y.sum().backward(retain_graph=True)
+    with pytest.raises(RuntimeError, match="twice"):
+        y.sum().backward()
+    y2 = mlp.swiglu_mlp(x, *w)
+    with pytest.raises(RuntimeError, match="create_graph"):
+        torch.autograd.grad(y2.sum(), x, create_graph=True)
