@@ -121,12 +121,13 @@ def bwd(dy, x, wg, wu, wd, saved, dx=None, dwg=None, dwu=None, dwd=None):
 
 
 def infer(x, wg, wu, wd, y=None, workspace=None, two_round=False):
-    """No-grad forward: only A[T,H] (the workspace) and Y[T,D] are written."""
+    """No-grad forward: only the workspace (A[T,H], plus fp32 partial sums
+    for T <= 64; ``infer_workspace_bytes`` bytes) and Y[T,D] are written."""
     x, wg, wu, wd = (t.contiguous() for t in (x, wg, wu, wd))
     T, D, H = _shapes(x, wg, wu, wd)
     y = _buf(y, (T, D), x, "y")
     if workspace is None:
-        workspace = torch.empty((T, H), dtype=x.dtype, device=x.device)
+        workspace = torch.empty(infer_workspace_bytes(T, D, H, x.dtype), dtype=torch.uint8, device=x.device)
     elif workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError(f"workspace must be a contiguous tensor on {x.device}")
     nbytes = workspace.numel() * workspace.element_size()

@@ -5,30 +5,28 @@
 // co-optimization", section "Summary"; its "Inference results" measure B=1,
 // S up to 256): time is set by how fast 3*D*H weights stream from HBM. The
 // output is cut into units of 16 weight columns; one workgroup per unit (688
-// units for H = 11008), so every CU has several units in flight, with
-// consecutive units on one XCD so that the four units sharing a 128-byte
-// line of a weight row share one L2. The four waves of a workgroup split K
-// and add their partial sums through LDS at the end; no global workspace,
-// so the no-grad path still writes only A and Y.
+// units for H = 11008), with consecutive units on one XCD so that the four
+// units sharing a 128-byte line of a weight row share one L2. The waves of a
+// workgroup (4 to 16, as many as LDS allows) split K and add their partial
+// sums through LDS at the end; no global workspace, so the no-grad path
+// still writes only A and Y.
 //
 // Per wave and K step of 32: the 32 x 16 weight slab (32-byte row segments)
 // and the activation tiles (16 tokens x 32 K each) are copied straight into a
-// wave-private LDS slot (buffer_load ... lds), NS slots deep; the weights are
-// read back transposed (ds_read_b64_tr_b16) as the 16 x 32 operand of
+// wave-private LDS slot (buffer_load ... lds), 3 or 4 slots deep; the weights
+// are read back transposed (ds_read_b64_tr_b16) as the 16 x 32 operand of
 // v_mfma_f32_16x16x32, the activations with ds_read_b128. The waves never
 // wait for one another inside the K loop. The loads are issued from inline
-// assembly and waited for explicitly (s_waitcnt vmcnt counts this wave's
-// loads in issue order): the compiler's own tracking of loads into LDS cannot
-// tell the slots apart and would wait for the newest load before every read.
+// assembly (dma16) and waited for explicitly: the compiler's own tracking of
+// loads into LDS cannot tell the slots apart and would wait for the newest
+// load before every read.
 #pragma once
 #include "gemm_tile.hpp"
 
 namespace swiglu {
 namespace skinny {
 
-constexpr int WAVES = 4;
 constexpr int KS = 32;     // K per step (one MFMA)
-constexpr int NS = 4;      // steps in flight per wave
 constexpr int SLAB = 1024; // 32 K rows x 16 columns x 2 B
 
 template <class E>

@@ -124,15 +124,19 @@ def cpu_baseline(inp, D, H, target_s):
 def infer_sweep(mlp, torch, dev, reps=20):
     """No-grad path at B=1, S in {1..256}, D/H in {1024/2816, 4096/11008}: device
     time per call (HIP events around the call only) with the 256 MB Infinity
-    Cache flushed before every timed call (a 1 GiB fill outside the events), and
-    HBM GB/s from the call's algorithmic bytes 2*(3*D*H + 2*T*D + 2*T*H).
+    Cache flushed before every timed call by reading a 1 GiB buffer outside the
+    events, and HBM GB/s from the call's algorithmic bytes
+    2*(3*D*H + 2*T*D + 2*T*H). A flush that writes leaves the caches full of
+    dirty lines whose write-back then competes with the call's reads; that
+    time is reported beside it (us_write_flush).
     Also the host-inclusive wall time of one call (Python binding, argument
     checks, two launches, completion), eagerly and as a replay of a HIP graph
     that captured the same call (checked bitwise against the eager output),
-    and the intermediate bytes the call needs (A workspace + Y)."""
+    and the intermediate bytes the call needs (workspace + Y; the workspace is
+    A, plus fp32 partial sums of the split-K kernels for S <= 64)."""
     from synth import INFER_DH, INFER_S, make_inputs
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     out = {}
     for D, H in INFER_DH:
         w = make_inputs(1, D, H, seed=77, dtype="bf16", with_dy=False)
@@ -141,25 +145,32 @@ def infer_sweep(mlp, torch, dev, reps=20):
         for S in INFER_S:
             X = make_inputs(S, D, H, seed=S, dtype="bf16", with_dy=False)["X"].to(dev)
             y = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(mlp.infer_workspace_bytes(S, D, H), dtype=torch.uint8, device=dev)
             for _ in range(3):
                 mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(reps)]
-            for a, b in ev:
-                flush.fill_(1)
-                a.record()
-                mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
-                b.record()
-            torch.cuda.synchronize()
-            us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-            med = us[len(us) // 2]
+            def device_us(write):
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(reps)]
+                for a, b in ev:
+                    if write:
+                        flush.fill_(1.0)
+                    else:
+                        flush.sum()
+                    a.record()
+                    mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+                    b.record()
+                torch.cuda.synchronize()
+                us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+                return us[len(us) // 2]
+
+            med = device_us(False)
+            med_w = device_us(True)
             nbytes = 2 * (3 * D * H + 2 * S * D + 2 * S * H)
 
             def wall(call):
                 ts = []
                 for _ in range(reps):
-                    flush.fill_(1)
+                    flush.sum()
                     torch.cuda.synchronize()
                     t0 = time.perf_counter()
                     call()
@@ -178,11 +189,12 @@ def infer_sweep(mlp, torch, dev, reps=20):
             same = bool(torch.equal(y, y_eager))
             graph_us = wall(graph.replay)
             del graph
-            rows[str(S)] = {"us": round(med, 2), "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+            rows[str(S)] = {"us": round(med, 2), "us_write_flush": round(med_w, 2),
+                            "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
                             "frac_hbm": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
                             "wall_us_eager": round(eager_us, 1), "wall_us_graph": round(graph_us, 1),
                             "graph_bitwise_equal": same,
-                            "intermediate_MiB": round(2 * (S * H + S * D) / 2**20, 3)}
+                            "intermediate_MiB": round((ws.numel() + 2 * S * D) / 2**20, 3)}
         out[f"{D}x{H}"] = rows
     del flush
     return out
@@ -221,6 +233,47 @@ def fp32_leg(mlp, torch, dev, steps=10, warmup=3):
     tf = 18.0 * T * D * H / (ms * 1e-3) / 1e12
     return {"config": {"D": D, "H": H, "B": B, "S": S, "T": T}, "dtype": "f32", "ms_per_step": round(ms, 3),
             "tflops": round(tf, 2), "peak_tflops": PEAK_FP32_TFLOPS, "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4)}
+
+
+def tp_shard_sweep(mlp, torch, dev, T, D, H, steps=5, warmup=2):
+    """Tensor-parallel shard shapes on one GPU: the same step at H/P for
+    P in {2, 4, 8} (Wg, Wu split by columns and Wd by rows; each GPU of a
+    TP group runs exactly this). Synthetic bf16 inputs of the headline's
+    scales; TFLOP/s = 18*T*D*(H/P) / mean step time."""
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(5)
+    bf = torch.bfloat16
+    X = torch.randn(T, D, device=dev, generator=g).to(bf)
+    dY = torch.randn(T, D, device=dev, generator=g).to(bf)
+    for P in (2, 4, 8):
+        h = H // P
+        Wg = (torch.randn(D, h, device=dev, generator=g) / D ** 0.5).to(bf)
+        Wu = (torch.randn(D, h, device=dev, generator=g) / D ** 0.5).to(bf)
+        Wd = (torch.randn(h, D, device=dev, generator=g) / H ** 0.5).to(bf)
+        y, saved = torch.empty((T, D), dtype=bf, device=dev), torch.empty((3, T, h), dtype=bf, device=dev)
+        dx = torch.empty((T, D), dtype=bf, device=dev)
+        dwg, dwu = (torch.empty((D, h), dtype=bf, device=dev) for _ in range(2))
+        dwd = torch.empty((h, D), dtype=bf, device=dev)
+
+        def step():
+            mlp.fwd(X, Wg, Wu, Wd, y=y, saved=saved)
+            mlp.bwd(dY, X, Wg, Wu, Wd, saved, dx=dx, dwg=dwg, dwu=dwu, dwd=dwd)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        tf = 18.0 * T * D * h / (ms * 1e-3) / 1e12
+        out[f"P={P}"] = {"H_shard": h, "ms_per_step": round(ms, 3), "tflops": round(tf, 1),
+                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del Wg, Wu, Wd, y, saved, dx, dwg, dwu, dwd
+    return out
 
 
 def ingest_traffic(fetch_csv, write_csv, copy_mib, command):
@@ -283,6 +336,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-infer", action="store_true", help="skip the no-grad (inference) sweep")
     ap.add_argument("--no-fp32", action="store_true", help="skip the true-IEEE fp32 run")
+    ap.add_argument("--no-tp", action="store_true", help="skip the tensor-parallel shard-shape sweep")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known traffic, used to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -387,8 +441,10 @@ def main():
     del g, X, Wg, Wu, Wd, dY, y, saved, dx, dwg, dwu, dwd
     if not args.no_fp32:
         out["fp32_ieee"] = fp32_leg(mlp, torch, dev)
+    if not args.no_tp:
+        out["tp_shards"] = tp_shard_sweep(mlp, torch, dev, T, D, H)
     if not args.no_infer:
-        out["infer"] = {"metric": "no-grad HBM GB/s (B=1, 256 MB cache flushed per call)",
+        out["infer"] = {"metric": "no-grad HBM GB/s (B=1, 256 MB cache flushed per call by a 1 GiB read)",
                         "peak_GBps": PEAK_HBM_GBS, "by_shape": infer_sweep(mlp, torch, dev)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, D, H, args.cpu_seconds)

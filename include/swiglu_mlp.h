@@ -89,9 +89,12 @@ typedef enum {
 /* Bytes of the saved A|G|U buffer: 3 * T * H * sizeof(dtype). 0 on bad args. */
 size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
 
-/* Bytes of the no-grad workspace: the A plane only, T * H * sizeof(dtype)
- * ("a dedicated no-grad path that does not save G/U", issue #1347, "Summary";
- * the page's table "Inference, BF16, B=1" equals A + Y). 0 on bad args. */
+/* Bytes of the no-grad workspace: the A plane, T * H * sizeof(dtype) ("a
+ * dedicated no-grad path that does not save G/U", issue #1347, "Summary";
+ * the page's table "Inference, BF16, B=1" equals A + Y at S = 256). For
+ * bf16/fp16 with 1 <= T <= 64 it also holds the fp32 partial sums of the
+ * split-K weight-streaming kernels (after A, 256-byte aligned): at most
+ * about 17 MB at D = 4096, H = 11008, T = 64. 0 on bad args. */
 size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
 
 /* Bytes of the backward workspace. Currently always 0 (no split-K fix-up). */
@@ -123,8 +126,9 @@ int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
                    int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream);
 
 /* No-grad forward: Y [T, D] from X and the weights; G and U are never
- * stored. workspace holds A (>= swiglu_mlp_infer_workspace_bytes bytes).
- * Y must not overlap the inputs or the workspace. */
+ * stored. workspace (>= swiglu_mlp_infer_workspace_bytes bytes) holds A and,
+ * for T <= 64, partial sums; its contents on entry do not matter. Y must not
+ * overlap the inputs or the workspace. */
 int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd,
                      void* Y, void* workspace, size_t workspace_bytes,
                      int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream);

@@ -38,7 +38,7 @@ def test_infer_graph_replay(mlp, S, D, H):
     banner(f"graph infer S={S} D={D} H={H}")
     g = to_dev(make_inputs(S, D, H, seed=31 + S, dtype="bf16", with_dy=False))
     y = torch.empty((S, D), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty((S, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mlp.infer_workspace_bytes(S, D, H), dtype=torch.uint8, device="cuda")
     mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], y=y, workspace=ws)
     torch.cuda.synchronize()
     ref = y.clone()

@@ -11,8 +11,9 @@ bf16 outputs differ between them. With SWIGLU_FLAG_TWO_ROUND:
     SiLU(g) lies within a few fp32 ulps of a 16-bit rounding tie;
   * the share of A that differs from the default one-round A is close to
     the pages' figure;
-  * the no-grad path returns the training Y bit for bit, on every kernel
-    family (few-token, small-T and ring);
+  * the no-grad path returns the training Y bit for bit where it runs the
+    same kernels (more than 64 tokens), and agrees within the bound where it
+    runs the split-K kernels;
   * the backward of a two-round forward meets the usual gradient bound;
   * in fp32 storage the two programs coincide.
 """
@@ -84,10 +85,18 @@ def test_two_round_epilogue(mlp, fmt, dt, T, D, H):
     if fmt == "bf16" and T * H >= 100000:
         assert 0.2 < diff < 0.35
     assert diff > 0.0
-    # no-grad path: same kernels' A, so the same Y
-    y_ng = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], two_round=True)
+    # no-grad path: above 64 tokens the same kernels, so the same Y; at most
+    # 64 tokens it runs the split-K kernels (another summation order), whose
+    # A in the workspace must then be the two-round program of their own sums
+    ws = torch.empty(mlp.infer_workspace_bytes(T, D, H, dt), dtype=torch.uint8, device="cuda")
+    y_ng = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], workspace=ws, two_round=True)
+    y_ng1 = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], workspace=ws, two_round=False)
     torch.cuda.synchronize()
-    assert torch.equal(y_ng, y2)
+    if T > 64:
+        assert torch.equal(y_ng, y2)
+    else:
+        assert nl2(f64(y_ng), f64(y2)) <= TOL[fmt]
+        assert not torch.equal(y_ng, y_ng1)
 
 
 def test_two_round_rate_and_backward_at_T16384(mlp):
