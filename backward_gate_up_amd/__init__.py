@@ -122,7 +122,7 @@ def bwd(dy, x, wg, wu, wd, saved, dx=None, dwg=None, dwu=None, dwd=None):
 
 def infer(x, wg, wu, wd, y=None, workspace=None, two_round=False):
     """No-grad forward: only the workspace (A[T,H], plus fp32 partial sums
-    for T <= 64; ``infer_workspace_bytes`` bytes) and Y[T,D] are written."""
+    for T <= 128; ``infer_workspace_bytes`` bytes) and Y[T,D] are written."""
     x, wg, wu, wd = (t.contiguous() for t in (x, wg, wu, wd))
     T, D, H = _shapes(x, wg, wu, wd)
     y = _buf(y, (T, D), x, "y")

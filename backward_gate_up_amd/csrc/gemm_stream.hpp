@@ -1,5 +1,5 @@
-// gemm_stream.hpp -- split-K weight streaming for the few-token no-grad
-// forward (T <= 64), gfx950.
+// gemm_stream.hpp -- split-K weight streaming for the no-grad forward with
+// few tokens (T <= 128), gfx950.
 //
 // With a handful of tokens the no-grad forward is a pass over the 3*D*H
 // weights ("[RFC] Full-pipeline SwiGLU MLP with forward/backward
@@ -11,12 +11,14 @@
 // across workgroups as well: workgroup (unit, split) streams K steps
 // [split * per, (split + 1) * per) of its 64 columns, its waves split that
 // range again, add their sums through LDS and write one fp32 partial block
-// to a workspace. A second kernel adds the partials of each output in split
-// order (deterministic) and applies the epilogue.
+// to a workspace (the waves' sums are added one 16-column block at a time,
+// so that they fit in LDS next to up to 8 token tiles). A second kernel adds
+// the partials of each output in split order (deterministic) and applies the
+// epilogue.
 //
 // Per wave and K step of 32: the 32 x 64 slab of each weight matrix (4 KiB:
 // four direct-to-LDS loads of 8 rows x 128 bytes) and the activation tiles
-// (16 tokens x 32 K each) land in a wave-private LDS slot, 3 or 4 slots deep,
+// (16 tokens x 32 K each) land in a wave-private LDS slot, 2 to 4 slots deep,
 // issued from inline assembly and waited for explicitly (dma16).
 #pragma once
 #include "gemm_skinny.hpp"

@@ -997,7 +997,7 @@ __global__ void __launch_bounds__((64 * SkinnyCfg<KIND, MT>::W)) skinny_gemm(con
 }
 
 // ---------------------------------------------------------------------------
-// Split-K weight streaming for the few-token no-grad forward (gemm_stream.hpp).
+// Split-K weight streaming for the no-grad forward, T <= 128 (gemm_stream.hpp).
 // KIND GATEUP: weights g.b0 = Wg, g.b1 = Wu; partial planes G, U.
 // KIND PLAIN: weights g.b0; one partial plane.
 // g.a0: activations [T, K] (K-contiguous); weights [K, N] (N-contiguous).
@@ -1008,7 +1008,7 @@ struct StreamCfg {
   static constexpr int NW = KIND == GATEUP ? 2 : 1;
   static constexpr int C = NW * 4 + MT;  // 1-KiB loads per step (= KiB per slot)
   static constexpr int W = 4;            // waves
-  static constexpr int NS = W * 4 * C <= 160 ? 4 : 3;
+  static constexpr int NS = W * 4 * C <= 160 ? 4 : (W * 3 * C <= 160 ? 3 : 2);
   static constexpr int BYTES = W * NS * C * 1024;
 };
 
@@ -1021,7 +1021,7 @@ __global__ void __launch_bounds__(256) stream_partial(const KArgs g, float* P, i
   constexpr int NW = Cfg::NW, C = Cfg::C, W = Cfg::W, NS = Cfg::NS;
   constexpr int SLOT = C * 1024;
   static_assert(Cfg::BYTES <= 160 * 1024, "LDS");
-  static_assert(Cfg::BYTES >= W * NW * 4 * MT * 1024, "partial sums must fit");
+  static_assert(Cfg::BYTES >= W * NW * MT * 1024, "one column block of partial sums must fit");
   static_assert((NS - 2) * C <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::BYTES];
 
@@ -1117,27 +1117,28 @@ __global__ void __launch_bounds__(256) stream_partial(const KArgs g, float* P, i
   }
   ring::wait_vmcnt<0>();  // the surplus steps' loads (zeros) have landed too
 
-  // add the waves' sums through LDS, then write this workgroup's partial
-  ring::lds_barrier();
-  constexpr int NB = NW * 4 * MT;  // 1-KiB blocks of f32x4 per wave
+  // add the waves' sums through LDS, one 16-column block at a time, and
+  // write this workgroup's partial
+  constexpr int NB = NW * MT;  // 1-KiB blocks of f32x4 per wave and column block
   char* part = lds + wave * (NB * 1024);
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
+  for (int c = 0; c < 4; ++c) {
+    ring::lds_barrier();  // the ring (or the previous block's sums) is no longer read
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int w = 0; w < NW; ++w)
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        *(f32x4_t*)(part + (((w * 4 + c) * MT + t) * 64 + lane) * 16) = acc[w][c][t];
-  ring::lds_barrier();
-  for (int blk = wave; blk < NB; blk += W) {
-    f32x4_t sum = f32x4_t{};
+      for (int t = 0; t < MT; ++t) *(f32x4_t*)(part + ((w * MT + t) * 64 + lane) * 16) = acc[w][c][t];
+    ring::lds_barrier();
+    for (int blk = wave; blk < NB; blk += W) {
+      f32x4_t sum = f32x4_t{};
 #pragma unroll
-    for (int v = 0; v < W; ++v) sum += *(const f32x4_t*)(lds + v * (NB * 1024) + (blk * 64 + lane) * 16);
-    const int w = blk / (4 * MT), c = (blk / MT) % 4, t = blk % MT;
-    // 16x16 output block: token t * 16 + lane % 16, columns 16 c + 4 (lane / 16) .. + 3
-    const int m = t * 16 + (lane & 15);
-    const int n = n0 + c * 16 + (lane >> 4) * 4;
-    if (m < T && n < N) *(f32x4_t*)(P + (((int64_t)split * NW + w) * T + m) * N + n) = sum;
+      for (int v = 0; v < W; ++v) sum += *(const f32x4_t*)(lds + v * (NB * 1024) + (blk * 64 + lane) * 16);
+      const int w = blk / MT, t = blk % MT;
+      // 16x16 output block: token t * 16 + lane % 16, columns 16 c + 4 (lane / 16) .. + 3
+      const int m = t * 16 + (lane & 15);
+      const int n = n0 + c * 16 + (lane >> 4) * 4;
+      if (m < T && n < N) *(f32x4_t*)(P + (((int64_t)split * NW + w) * T + m) * N + n) = sum;
+    }
   }
 }
 
@@ -1289,7 +1290,7 @@ static int launch_skinny(KArgs a, int64_t T, int64_t ncols, hipStream_t stream) 
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
-// Split-K streaming launch (no-grad, 16-bit, T <= 64): partials into P, then
+// Split-K streaming launch (no-grad, 16-bit, T <= 128): partials into P, then
 // the reduction with the epilogue; timed as one stage.
 template <class E, int KIND, int MT>
 static void launch_stream_mt(const KArgs& a, int grid, int splits, float* P, hipStream_t stream) {
@@ -1303,17 +1304,20 @@ static int launch_stream(KArgs a, int64_t T, int64_t ncols, float* P, hipStream_
   StageScope scope(STAGE, stream);
   if (T <= 16) launch_stream_mt<E, KIND, 1>(a, units * splits, splits, P, stream);
   else if (T <= 32) launch_stream_mt<E, KIND, 2>(a, units * splits, splits, P, stream);
-  else launch_stream_mt<E, KIND, 4>(a, units * splits, splits, P, stream);
+  else if (T <= 64) launch_stream_mt<E, KIND, 4>(a, units * splits, splits, P, stream);
+  else launch_stream_mt<E, KIND, 8>(a, units * splits, splits, P, stream);
   if (hipGetLastError() != hipSuccess) return SWIGLU_ERR_LAUNCH;
   const int64_t nq = T * (ncols / 4);
   hipLaunchKernelGGL((stream_reduce<E, KIND>), dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream, a, P, splits);
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
-// Tokens up to which the forward runs on the weight-streaming kernels.
+// Tokens up to which the forward runs on the weight-streaming kernels
+// (training: few_t; no-grad, which has a workspace for partial sums: stream_t).
 static inline bool few_t(int64_t T) { return T <= 64; }
+static inline bool stream_t(int64_t T) { return T <= 128; }
 
-// fp32 partials of the split-K no-grad path (16-bit, T <= 64): the larger of
+// fp32 partials of the split-K no-grad path (16-bit, T <= 128): the larger of
 // the gate/up (2 planes of [T, H]) and down ([T, D]) stages, placed after the
 // A plane in the no-grad workspace (256-byte aligned).
 static inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -1349,8 +1353,10 @@ struct Path {
     a.N = (int)H;
     a.store_gu = store_gu ? 1 : 0;
     a.two_round = two_round ? 1 : 0;
-    if constexpr (E::kBytes == 2)
-      if (few_t(T)) return P ? launch_stream<E, GATEUP, STAGE>(a, T, H, P, s) : launch_skinny<E, GATEUP, STAGE>(a, T, H, s);
+    if constexpr (E::kBytes == 2) {
+      if (P && stream_t(T)) return launch_stream<E, GATEUP, STAGE>(a, T, H, P, s);
+      if (few_t(T)) return launch_skinny<E, GATEUP, STAGE>(a, T, H, s);
+    }
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(H, 128);
@@ -1372,8 +1378,10 @@ struct Path {
     a.ldc = D;
     a.M = (int)T;
     a.N = (int)D;
-    if constexpr (E::kBytes == 2)
-      if (few_t(T)) return P ? launch_stream<E, PLAIN, STAGE>(a, T, D, P, s) : launch_skinny<E, PLAIN, STAGE>(a, T, D, s);
+    if constexpr (E::kBytes == 2) {
+      if (P && stream_t(T)) return launch_stream<E, PLAIN, STAGE>(a, T, D, P, s);
+      if (few_t(T)) return launch_skinny<E, PLAIN, STAGE>(a, T, D, s);
+    }
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(D, 256);
@@ -1574,7 +1582,7 @@ template <class E>
 static int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws, int64_t T,
                      int64_t D, int64_t H, bool two_round, hipStream_t s) {
   char* Ap = (char*)ws;
-  float* P = (E::kBytes == 2 && few_t(T)) ? (float*)(Ap + align256((size_t)T * H * E::kBytes)) : nullptr;
+  float* P = (E::kBytes == 2 && stream_t(T)) ? (float*)(Ap + align256((size_t)T * H * E::kBytes)) : nullptr;
   int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, P, s);
   if (rc) return rc;
   return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, P, s);
@@ -1596,7 +1604,7 @@ size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dty
   size_t e = elt_bytes(dtype);
   if (!e || T < 0 || D <= 0 || H <= 0) return 0;
   const size_t a = (size_t)T * (size_t)H * e;
-  if (e == 2 && T > 0 && few_t(T)) return align256(a) + stream_partial_bytes(T, D, H);
+  if (e == 2 && T > 0 && stream_t(T)) return align256(a) + stream_partial_bytes(T, D, H);
   return a;
 }
 

@@ -133,7 +133,7 @@ def infer_sweep(mlp, torch, dev, reps=20):
     checks, two launches, completion), eagerly and as a replay of a HIP graph
     that captured the same call (checked bitwise against the eager output),
     and the intermediate bytes the call needs (workspace + Y; the workspace is
-    A, plus fp32 partial sums of the split-K kernels for S <= 64)."""
+    A, plus fp32 partial sums of the split-K kernels for S <= 128)."""
     from synth import INFER_DH, INFER_S, make_inputs
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB

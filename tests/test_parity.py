@@ -150,7 +150,7 @@ def test_no_grad_path(mlp, D, H):
         err = nl2(f64(y), O.infer(X.float().numpy(), f["Wg"], f["Wu"], f["Wd"]))
         banner(f"infer D={D} S={S}: {err:.2e}")
         assert err <= 1e-2
-        if S > 64:
+        if S > 128:
             # same tiles, same order: the no-grad Y equals the training Y bitwise
             assert torch.equal(y, y_train)
         else:
@@ -161,9 +161,10 @@ def test_no_grad_path(mlp, D, H):
 
 
 @pytest.mark.parametrize("T,D,H", [(1, 136, 200), (17, 264, 520), (40, 200, 136), (64, 520, 264),
-                                   (3, 64, 64), (33, 1032, 2824)])
+                                   (3, 64, 64), (33, 1032, 2824), (65, 264, 520), (100, 1032, 2824),
+                                   (128, 200, 136)])
 def test_no_grad_split_k_ragged(mlp, T, D, H):
-    """The split-K streaming kernels (bf16, T <= 64) at K not a multiple of
+    """The split-K streaming kernels (bf16, T <= 128) at K not a multiple of
     32 and N not a multiple of 64: ragged last K steps and column units."""
     inp = make_inputs(T, D, H, seed=T * 7 + D, dtype="bf16", with_dy=False)
     g = to_dev(inp)
