@@ -1383,9 +1383,19 @@ struct Path {
       if (few_t(T)) return launch_skinny<E, PLAIN, STAGE>(a, T, D, s);
     }
     if (small_t(T)) {
+      // 64-row tiles; the widest N tile that still gives 256 workgroups (the
+      // down projection has only D / 256 tiles of 256 columns per row block)
       a.tiles_m = cdiv(T, 64);
-      a.tiles_n = cdiv(D, 256);
-      return launch<E, 64, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
+      if (a.tiles_m * cdiv(D, 256) >= 256) {
+        a.tiles_n = cdiv(D, 256);
+        return launch<E, 64, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
+      }
+      if (a.tiles_m * cdiv(D, 128) >= 256) {
+        a.tiles_n = cdiv(D, 128);
+        return launch<E, 64, 128, KC, MC, PLAIN, STAGE>(a, 1, s);
+      }
+      a.tiles_n = cdiv(D, 64);
+      return launch<E, 64, 64, KC, MC, PLAIN, STAGE>(a, 1, s);
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(D, 256);
