@@ -150,9 +150,10 @@ const char* swiglu_mlp_status_string(int status);
  *   4 [dWg | dWu] = X^T [dG | dU]      5 dI single accumulator
  *   6 no-grad gate/up (A only)         7 no-grad down projection
  *   8 stages 3 + 2 in one launch       9 stages 4 + 5 in one launch
- * (for T > 512 the backward runs as launches 8 and 9: the long-K weight-
- * gradient tiles are dispatched first and the short tiles of the other stage
- * fill in behind them.)
+ * (bf16/fp16 run every stage as its own launch; in fp32 with T > 512 the
+ * backward runs as launches 8 and 9, where the long-K weight-gradient tiles
+ * are dispatched first and the short tiles of the other stage fill in
+ * behind them.)
  * swiglu_mlp_timer_start(capacity) makes every later launch of a stage record
  * a HIP event pair around it on the launch stream, up to `capacity` launches
  * per stage (events are created here; returns a status). swiglu_mlp_timer_stop

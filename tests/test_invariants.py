@@ -94,3 +94,38 @@ def test_device_errors_raise(mlp):
     with pytest.raises(SwiGLUError, match="ALIGN"):
         buf = torch.empty(16 * 64 + 1, dtype=torch.bfloat16, device="cuda")
         mlp.fwd(inp["X"], inp["Wg"], inp["Wu"], inp["Wd"], y=buf[1:].view(16, 64))
+
+
+@pytest.mark.parametrize("T", [8, 100, 300, 600])
+def test_nan_and_inf_propagate(mlp, T):
+    """A non-finite input value reaches exactly the outputs that depend on it,
+    with no trap, on every kernel family (few-token, split-K no-grad, 64-row
+    tiles, ring). NaN in one row of X poisons that row of Y and dI and every
+    weight gradient; the other rows stay finite. +Inf in one gate value
+    (through Wg) takes the fast and the IEEE logistic paths."""
+    D, H, bad = 256, 384, 3
+    inp = make_inputs(T, D, H, seed=T + 5, dtype="bf16")
+    g = to_dev(inp)
+    g["X"][bad, 7] = float("nan")
+    out = run_train(mlp, g)
+    rows = torch.arange(T, device="cuda") != bad
+    for k in ("Y", "dI"):
+        assert torch.isnan(out[k][bad]).all(), k
+        assert torch.isfinite(out[k][rows]).all(), k
+    for k in ("dWg", "dWu", "dWd"):
+        assert torch.isnan(out[k]).any(), k
+    y_ng = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"])
+    torch.cuda.synchronize()
+    assert torch.isnan(y_ng[bad]).all() and torch.isfinite(y_ng[rows]).all()
+    # +-Inf gate pre-activations: one column of Wg set to +Inf reaches every
+    # row's g in that hidden unit; SiLU(+Inf) = +Inf, SiLU(-Inf) = -Inf * 0
+    g = to_dev(inp)
+    g["Wg"][:, 5] = float("inf")
+    y, saved = mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"])
+    torch.cuda.synchronize()
+    G, A = saved[1][:, 5].float(), saved[0][:, 5].float()
+    assert torch.isinf(G).all() or torch.isnan(G).any()
+    assert not torch.isfinite(A).all()
+    other = torch.ones(H, dtype=torch.bool, device="cuda")
+    other[5] = False
+    assert torch.isfinite(saved[0][:, other]).all()
