@@ -1468,7 +1468,7 @@ struct Path {
   // T > 512. bf16/fp16: the four ring launches (stages 2, 3, 4, 5). fp32 on
   // the register-staged engine: paired launches, {dWd (long K = T), dA +
   // dSwiGLU} as stage 8, then {dWg | dWu (long K = T), dI} as stage 9.
-  static int bwd_paired(KArgs dgu, KArgs dwd, KArgs dwgu, KArgs dx, int64_t T, int64_t D, int64_t H,
+  static int bwd_large(KArgs dgu, KArgs dwd, KArgs dwgu, KArgs dx, int64_t T, int64_t D, int64_t H,
                         hipStream_t s) {
     dgu.tiles_m = cdiv(T, 256);
     dgu.tiles_n = cdiv(H, 256);
@@ -1569,7 +1569,7 @@ static int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
   KArgs dwgu = Path<E>::args_dwgu(X, Gp, Up, dWg, dWu, T, D, H);
   KArgs dx = Path<E>::args_dx(Gp, Up, Wg, Wu, dX, T, D, H);
   if (small_t(T)) return Path<E>::bwd_separate(dgu, dwd, dwgu, dx, T, D, H, s);
-  return Path<E>::bwd_paired(dgu, dwd, dwgu, dx, T, D, H, s);
+  return Path<E>::bwd_large(dgu, dwd, dwgu, dx, T, D, H, s);
 }
 
 template <class E>
