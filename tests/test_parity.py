@@ -137,6 +137,42 @@ def test_headline_T65536_sampled(mlp):
         assert v <= 1e-2, (k, v)
 
 
+def test_planes_over_2GiB_sampled(mlp):
+    """T = 131072, D = 4096, H = 11008: each [T, H] plane of the saved buffer
+    is 2.9 GB, past the 2 GiB range of one buffer descriptor (the kernels
+    rebase their descriptors per tile and K stage). Sampled rows on both
+    sides of byte offset 2^31 in the planes, and sampled hidden units of the
+    weight gradients, against the oracle."""
+    T, D, H = 131072, 4096, 11008
+    banner(f"T={T}: inputs")
+    inp = make_inputs(T, D, H, seed=77, dtype="bf16")
+    g = to_dev(inp)
+    banner(f"T={T}: GPU fwd+bwd")
+    y, saved = mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"])
+    first_past = (1 << 31) // (H * 2) + 1  # first row starting past 2 GiB in a plane
+    rows = np.array([0, 255, first_past - 1, first_past, first_past + 300, T - 257, T - 1])
+    G_s, U_s, A_s = (saved[i][rows].clone() for i in (1, 2, 0))
+    dx, dwg, dwu, dwd = mlp.bwd(g["dY"], g["X"], g["Wg"], g["Wu"], g["Wd"], saved)
+    dG_s, dU_s = saved[1][rows].clone(), saved[2][rows].clone()
+    torch.cuda.synchronize()
+    del g, saved
+    f = _np(inp)
+    banner(f"T={T}: oracle rows and hidden units")
+    r = O.rows(rows, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
+    e = {"Y": nl2(f64(y[rows]), r["Y"]), "dI": nl2(f64(dx[rows]), r["dI"]), "G": nl2(f64(G_s), r["G"]),
+         "U": nl2(f64(U_s), r["U"]), "dG": nl2(f64(dG_s), r["dG"]), "dU": nl2(f64(dU_s), r["dU"])}
+    a_ref = O.round_to(O.epilogue_fwd(f64(G_s), f64(U_s)), "bf16")
+    assert int(O.ulp_distance(f64(A_s), a_ref, "bf16").max()) <= 1
+    hs = np.array([0, 4999, 11007])
+    c = O.cols(hs, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
+    e["dWg"] = nl2(f64(dwg[:, hs]), c["dWg"])
+    e["dWu"] = nl2(f64(dwu[:, hs]), c["dWu"])
+    e["dWd"] = nl2(f64(dwd[hs, :]), c["dWd"])
+    banner(f"T={T}: " + " ".join(f"{k}={v:.2e}" for k, v in e.items()))
+    for k, v in e.items():
+        assert v <= 1e-2, (k, v)
+
+
 @pytest.mark.parametrize("D,H", [(1024, 2816), (4096, 11008)])
 def test_no_grad_path(mlp, D, H):
     wts = make_inputs(1, D, H, seed=2024 + D, dtype="bf16", with_dy=False)
