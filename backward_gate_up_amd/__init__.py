@@ -21,7 +21,7 @@ from . import _lib as _L
 from ._lib import SwiGLUError, STAGE_NAMES, NUM_STAGES  # noqa: F401
 
 __all__ = ["fwd", "bwd", "infer", "SwiGLUMLPFunction", "swiglu_mlp", "SwiGLUMLP", "saved_bytes",
-           "infer_workspace_bytes", "SwiGLUError", "StageTimer"]
+           "infer_workspace_bytes", "bwd_workspace_bytes", "SwiGLUError", "StageTimer"]
 
 _DT = {torch.bfloat16: _L.BF16, torch.float16: _L.FP16, torch.float32: _L.FP32}
 
@@ -101,9 +101,14 @@ def fwd(x, wg, wu, wd, y=None, saved=None, two_round=False):
     return y, saved
 
 
-def bwd(dy, x, wg, wu, wd, saved, dx=None, dwg=None, dwu=None, dwd=None):
+def bwd_workspace_bytes(T, D, H, dtype=torch.bfloat16):
+    return _L.lib().swiglu_mlp_bwd_workspace_bytes(T, D, H, _DT[dtype])
+
+
+def bwd(dy, x, wg, wu, wd, saved, dx=None, dwg=None, dwu=None, dwd=None, workspace=None):
     """Full backward. Overwrites the G/U planes of ``saved`` with dG/dU.
-    Returns (dX, dWg, dWu, dWd)."""
+    Returns (dX, dWg, dWu, dWd). ``workspace``: at least
+    ``bwd_workspace_bytes`` bytes (allocated here when None and needed)."""
     dy, x, wg, wu, wd = (t.contiguous() for t in (dy, x, wg, wu, wd))
     T, D, H = _shapes(x, wg, wu, wd)
     if tuple(dy.shape) != (T, D) or dy.dtype != x.dtype or dy.device != x.device:
@@ -113,8 +118,14 @@ def bwd(dy, x, wg, wu, wd, saved, dx=None, dwg=None, dwu=None, dwd=None):
         raise ValueError("saved must be the contiguous [3, T, H] buffer returned by fwd")
     dx, dwg, dwu, dwd = (_buf(dx, (T, D), x, "dx"), _buf(dwg, (D, H), x, "dwg"),
                          _buf(dwu, (D, H), x, "dwu"), _buf(dwd, (H, D), x, "dwd"))
+    need = bwd_workspace_bytes(T, D, H, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    elif workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {x.device}")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _L.lib().swiglu_mlp_bwd(_p(dy), _p(x), _p(wg), _p(wu), _p(wd), _p(saved),
-                                 _p(dx), _p(dwg), _p(dwu), _p(dwd), None, 0,
+                                 _p(dx), _p(dwg), _p(dwu), _p(dwd), _p(workspace), ws_bytes,
                                  T, D, H, _dt(x), _stream(x.device))
     _check(rc, "swiglu_mlp_bwd")
     return dx, dwg, dwu, dwd

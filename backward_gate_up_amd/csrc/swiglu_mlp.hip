@@ -52,6 +52,8 @@ struct KArgs {
   int planes;      // PLAIN: number of (B source, output) planes (1 or 2)
   int group_m;     // M-tiles per group of the tile walk (tile_coords); 0 = 8
   int two_round;   // GATEUP: A = rnd(rnd(SiLU(g)) * u) instead of rnd(SiLU(g) * u)
+  float* P;        // PLAIN, split K: fp32 partials [ksplit][planes][M][N] (else nullptr)
+  int kchunk;      // PLAIN, split K: K stages per split (split = blockIdx.y)
 };
 
 // Logistic function sigma(g) = 1 / (1 + exp(-g)) in fp32, from a stored gate
@@ -512,7 +514,7 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
 // compiler wait for exactly the stage a read needs.
 template <class E, int AL, int BL, int KIND>
 __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, char* st2, char* st3, int bid,
-                                          int bz) {
+                                          int bz, int ks = 0) {
   using namespace ring;
   static_assert(E::kBytes == 2, "the ring pipeline is for bf16/fp16");
   // the wave index is uniform within a wave; readfirstlane lets the compiler
@@ -548,7 +550,10 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   da.init(A, m0, wave, lane);
   db.init(B, n0, wave, lane);
   const int nk1 = (A.k + BK - 1) / BK;
-  const int nk = (KIND == DX) ? 2 * nk1 : nk1;
+  // split K (PLAIN with partials): stages [sb, sb + nk) of the K loop
+  const bool split = KIND == PLAIN && g.P != nullptr;
+  const int sb = split ? ks * g.kchunk : 0;
+  const int nk = (KIND == DX) ? 2 * nk1 : (split ? (nk1 - sb < g.kchunk ? nk1 - sb : g.kchunk) : nk1);
   char* st[4] = {st0, st1, st2, st3};
 
   auto issue_a = [&](int s, char* stg) {
@@ -556,9 +561,9 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
       const bool h = s >= nk1;
       da.issue_kc(h ? g.a1 : g.a0, m0, (h ? s - nk1 : s) * BK, stg, wave, lane);
     } else if constexpr (AL == KC) {
-      da.issue_kc(A, m0, s * BK, stg, wave, lane);
+      da.issue_kc(A, m0, (sb + s) * BK, stg, wave, lane);
     } else {
-      da.issue_mc(A, m0, A, m0 + 128, s * BK, stg, wave);
+      da.issue_mc(A, m0, A, m0 + 128, (sb + s) * BK, stg, wave);
     }
   };
   auto issue_b = [&](int s, char* stg) {
@@ -566,11 +571,11 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
       const bool h = s >= nk1;
       db.issue_kc(h ? g.b1 : g.b0, n0, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
     } else if constexpr (BL == KC) {
-      db.issue_kc(B, n0, s * BK, stg + OPB, wave, lane);
+      db.issue_kc(B, n0, (sb + s) * BK, stg + OPB, wave, lane);
     } else if constexpr (KIND == GATEUP) {
       db.issue_mc(g.b0, n0, g.b1, n0, s * BK, stg + OPB, wave);
     } else {
-      db.issue_mc(B, n0, B, n0 + 128, s * BK, stg + OPB, wave);
+      db.issue_mc(B, n0, B, n0 + 128, (sb + s) * BK, stg + OPB, wave);
     }
   };
   auto issue = [&](int s, char* stg) {
@@ -633,6 +638,27 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
       f0.read(slot(s + 1), a_rows, b_rows, 0, lane);
     }
     f1.mma(acc);
+  }
+  if constexpr (KIND == PLAIN) {
+    if (split) {
+      // fp32 partial of this K split; lane holds 4 consecutive columns
+      float* P = g.P + ((int64_t)ks * g.planes + bz) * g.M * (int64_t)g.N;
+      const int ml = lane & 31, nl = (lane >> 5) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + a_rows[i] + ml;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + b_rows[j] + q * 8 + nl;
+            if (m < g.M && n < g.N)
+              *(f32x4_t*)(P + (int64_t)m * g.N + n) =
+                  f32x4_t{acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
+          }
+      }
+      return;
+    }
   }
   ring_epilogue<E, KIND>(g, C, acc, m0, n0, wm, wn, lane, slot(wave));
 }
@@ -784,9 +810,9 @@ constexpr int ring_variant() {
 }
 
 template <class E, int AL, int BL, int KIND>
-__device__ __forceinline__ void any_ring_tile(const KArgs& g, char* const (&R)[5], int bid, int bz) {
+__device__ __forceinline__ void any_ring_tile(const KArgs& g, char* const (&R)[5], int bid, int bz, int ks) {
   if constexpr (ring_variant<AL, BL>() == 5) ring5_tile<E, AL, BL, KIND>(g, R, bid, bz);
-  else ring_tile<E, AL, BL, KIND>(g, R[0], R[1], R[2], R[3], bid, bz);
+  else ring_tile<E, AL, BL, KIND>(g, R[0], R[1], R[2], R[3], bid, bz, ks);
 }
 
 // Four 32 KiB LDS arrays, and a fifth when a five-array ring runs.
@@ -807,7 +833,7 @@ template <class E, int AL, int BL, int KIND, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ring_gemm(const KArgs g) {
   SWIGLU_RING_LDS((ring_variant<AL, BL>() == 5))
-  any_ring_tile<E, AL, BL, KIND>(g, R, blockIdx.x, blockIdx.z);
+  any_ring_tile<E, AL, BL, KIND>(g, R, blockIdx.x, blockIdx.z, blockIdx.y);
 }
 
 
@@ -1172,6 +1198,26 @@ __global__ void __launch_bounds__(256) stream_reduce(const KArgs g, const float*
   }
 }
 
+// Sum of the K-split partials of a PLAIN ring launch, in split order
+// (deterministic): C = rnd(sum over s of P[s]), for 1 or 2 output planes (c0,
+// c1). One thread per 4 consecutive outputs of a row.
+template <class E>
+__global__ void __launch_bounds__(256) splitk_reduce(const float* P, int ksplit, int planes, int M, int N, char* c0,
+                                                     char* c1, int64_t ldc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = (int64_t)M * (N / 4);
+  if (i >= per * planes) return;
+  const int z = (int)(i / per);
+  const int64_t r = i - z * per;
+  const int m = (int)(r / (N / 4)), n = (int)(r % (N / 4)) * 4;
+  f32x4_t sum = f32x4_t{};
+  for (int s = 0; s < ksplit; ++s) sum += *(const f32x4_t*)(P + (((int64_t)s * planes + z) * M + m) * N + n);
+  typename E::vec4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = E::from_f32(sum[e]);
+  *(typename E::vec4*)((z ? c1 : c0) + ((int64_t)m * ldc + n) * E::kBytes) = v;
+}
+
 // Fill kernel (used to clear weight gradients when T = 0 would otherwise
 // leave them unwritten; a kernel rather than a memset so that callers may
 // capture the path in a graph).
@@ -1253,6 +1299,57 @@ static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
 
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// K splits for a weight-gradient ring launch (K = T) with under half as many
+// output tiles as CUs: enough splits for about one workgroup per CU, each at
+// least 16 K stages. With 128 or more tiles, writing and adding the fp32
+// partials cost more than the idle CUs (measured at D = 2048, H = 5632 and at
+// H = 1376), so those run unsplit.
+static inline void splitk_plan(int tiles, int64_t K, int& splits, int& kchunk) {
+  const int nk = cdiv(K, ring::BK);
+  splits = 1;
+  kchunk = nk;
+  if (tiles >= 128) return;
+  int s = cdiv(256, tiles);
+  if (s > nk / 16) s = nk / 16;
+  if (s <= 1) return;
+  kchunk = cdiv(nk, s);
+  splits = cdiv(nk, kchunk);
+}
+
+// Ring launch of a PLAIN stage, split over K when splitk_plan says so: fp32
+// partials into P, then splitk_reduce into the outputs; timed as one stage.
+template <class E, int AL, int BL, int STAGE>
+static int launch_ring_splitk(KArgs a, int grid_z, float* P, hipStream_t stream) {
+  int splits, kchunk;
+  splitk_plan(a.tiles_m * a.tiles_n * grid_z, a.a0.k, splits, kchunk);
+  if (splits <= 1) {
+    a.P = nullptr;
+    return launch_ring<E, AL, BL, PLAIN, STAGE>(a, grid_z, stream);
+  }
+  const int nb = a.tiles_m * a.tiles_n;
+  a.planes = grid_z;
+  a.group_m = kRingGroupM;
+  a.P = P;
+  a.kchunk = kchunk;
+  StageScope scope(STAGE, stream);
+  hipLaunchKernelGGL((ring_gemm<E, AL, BL, PLAIN, STAGE>), dim3(nb, splits, grid_z), dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return SWIGLU_ERR_LAUNCH;
+  const int64_t nq = (int64_t)grid_z * a.M * (a.N / 4);
+  hipLaunchKernelGGL((splitk_reduce<E>), dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream, (const float*)P,
+                     splits, grid_z, a.M, a.N, a.c0, a.c1, a.ldc);
+  return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+// fp32 partial bytes of the split weight-gradient launches (bf16/fp16, T >
+// 512): the larger of dWd ([H, D]) and [dWg | dWu] (2 x [D, H]).
+static inline size_t splitk_bytes(int64_t T, int64_t D, int64_t H) {
+  int sd, sg, kc;
+  splitk_plan(cdiv(H, 256) * cdiv(D, 256), T, sd, kc);
+  splitk_plan(cdiv(D, 256) * cdiv(H, 256) * 2, T, sg, kc);
+  const size_t pd = sd > 1 ? (size_t)sd * H * D * 4 : 0, pg = sg > 1 ? (size_t)sg * 2 * D * H * 4 : 0;
+  return pd > pg ? pd : pg;
+}
 
 // Few-token launch: one workgroup per 16 output columns.
 template <class E, int KIND, int STAGE>
@@ -1468,8 +1565,8 @@ struct Path {
   // T > 512. bf16/fp16: the four ring launches (stages 2, 3, 4, 5). fp32 on
   // the register-staged engine: paired launches, {dWd (long K = T), dA +
   // dSwiGLU} as stage 8, then {dWg | dWu (long K = T), dI} as stage 9.
-  static int bwd_large(KArgs dgu, KArgs dwd, KArgs dwgu, KArgs dx, int64_t T, int64_t D, int64_t H,
-                        hipStream_t s) {
+  static int bwd_large(KArgs dgu, KArgs dwd, KArgs dwgu, KArgs dx, int64_t T, int64_t D, int64_t H, float* P,
+                       hipStream_t s) {
     dgu.tiles_m = cdiv(T, 256);
     dgu.tiles_n = cdiv(H, 256);
     dx.tiles_m = cdiv(T, 256);
@@ -1479,8 +1576,8 @@ struct Path {
       // short-K stages with the long-K weight gradients on the ring engine
       int rc;
       if ((rc = launch_ring<E, KC, KC, DSWIGLU, 2>(dgu, 1, s))) return rc;
-      if ((rc = launch_ring<E, MC, MC, PLAIN, 3>(dwd, 1, s))) return rc;
-      if ((rc = launch_ring<E, MC, MC, PLAIN, 4>(dwgu, 2, s))) return rc;
+      if ((rc = launch_ring_splitk<E, MC, MC, 3>(dwd, 1, P, s))) return rc;
+      if ((rc = launch_ring_splitk<E, MC, MC, 4>(dwgu, 2, P, s))) return rc;
       return launch_ring<E, KC, KC, DX, 5>(dx, 1, s);
     } else {
       int rc = launch_pair<E, MC, MC, PLAIN, KC, KC, DSWIGLU, 8>(dwd, dgu, s);
@@ -1559,7 +1656,8 @@ static int run_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd
 
 template <class E>
 static int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
-                   void* dX, void* dWg, void* dWu, void* dWd, int64_t T, int64_t D, int64_t H, hipStream_t s) {
+                   void* dX, void* dWg, void* dWu, void* dWd, float* P, int64_t T, int64_t D, int64_t H,
+                   hipStream_t s) {
   const size_t plane = (size_t)T * H * E::kBytes;
   char* Ap = (char*)saved;
   char* Gp = Ap + plane;
@@ -1569,7 +1667,7 @@ static int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
   KArgs dwgu = Path<E>::args_dwgu(X, Gp, Up, dWg, dWu, T, D, H);
   KArgs dx = Path<E>::args_dx(Gp, Up, Wg, Wu, dX, T, D, H);
   if (small_t(T)) return Path<E>::bwd_separate(dgu, dwd, dwgu, dx, T, D, H, s);
-  return Path<E>::bwd_large(dgu, dwd, dwgu, dx, T, D, H, s);
+  return Path<E>::bwd_large(dgu, dwd, dwgu, dx, T, D, H, P, s);
 }
 
 template <class E>
@@ -1602,7 +1700,11 @@ size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dty
   return a;
 }
 
-size_t swiglu_mlp_bwd_workspace_bytes(int64_t, int64_t, int64_t, int) { return 0; }
+size_t swiglu_mlp_bwd_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype) {
+  const size_t e = elt_bytes(dtype);
+  if (e != 2 || T <= 0 || D <= 0 || H <= 0 || small_t(T)) return 0;
+  return splitk_bytes(T, D, H);
+}
 
 int swiglu_mlp_fwd_ex(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
                       int64_t D, int64_t H, int dtype, unsigned flags, hipStream_t stream) {
@@ -1636,20 +1738,21 @@ int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd
 int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
                    void* dX, void* dWg, void* dWu, void* dWd, void* workspace, size_t workspace_bytes, int64_t T,
                    int64_t D, int64_t H, int dtype, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   size_t e = elt_bytes(dtype);
   if (!e) return SWIGLU_ERR_DTYPE;
   int rc = check_shape(T, D, H);
   if (rc) return rc;
   const size_t td = (size_t)T * D * e, dh = (size_t)D * H * e;
+  const size_t need = swiglu_mlp_bwd_workspace_bytes(T, D, H, dtype);
   Range in[] = {{dY, td}, {X, td}, {Wg, dh}, {Wu, dh}, {Wd, dh}, {saved, 3 * (size_t)T * H * e}};
-  Range out[] = {{dX, td}, {dWg, dh}, {dWu, dh}, {dWd, dh}};
+  Range out[] = {{dX, td}, {dWg, dh}, {dWu, dh}, {dWd, dh}, {workspace, need}};
   if ((rc = check_ptrs(in, 6)) || (rc = check_ptrs(out, 4))) return rc;
-  for (int i = 0; i < 4; ++i) {
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SWIGLU_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return SWIGLU_ERR_ALIGN;
+  for (int i = 0; i < 5; ++i) {
     for (auto& r : in)
       if (overlap(out[i], r)) return SWIGLU_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < 5; ++j)
       if (overlap(out[i], out[j])) return SWIGLU_ERR_ALIAS;
   }
   if ((rc = check_device())) return rc;
@@ -1660,9 +1763,12 @@ int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
     return zero_fill(dWd, dh, stream);
   }
   switch (dtype) {
-    case SWIGLU_BF16: return run_bwd<Bf16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, T, D, H, stream);
-    case SWIGLU_FP16: return run_bwd<Fp16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, T, D, H, stream);
-    default: return run_bwd<Fp32>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, T, D, H, stream);
+    case SWIGLU_BF16:
+      return run_bwd<Bf16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, (float*)workspace, T, D, H, stream);
+    case SWIGLU_FP16:
+      return run_bwd<Fp16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, (float*)workspace, T, D, H, stream);
+    default:
+      return run_bwd<Fp32>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, nullptr, T, D, H, stream);
   }
 }
 

@@ -97,7 +97,11 @@ size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
  * about 34 MB at D = 4096, H = 11008, T = 128. 0 on bad args. */
 size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
 
-/* Bytes of the backward workspace. Currently always 0 (no split-K fix-up). */
+/* Bytes of the backward workspace: fp32 partial sums of the weight-gradient
+ * GEMMs (K = T) when they have under half as many output tiles as the GPU
+ * has CUs and are split over K (bf16/fp16, T > 512: for example D = 1024,
+ * H = 2816, or H = 1376 at D = 4096). 0 when no split is needed, as at
+ * D = 4096, H = 11008, and for fp32. 0 on bad args. */
 size_t swiglu_mlp_bwd_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
 
 /* Forward for training. Reads X, Wg, Wu, Wd; writes Y [T, D] and the saved
@@ -118,8 +122,9 @@ int swiglu_mlp_fwd_ex(const void* X, const void* Wg, const void* Wu, const void*
  * swiglu_mlp_fwd with the same inputs; writes dX [T, D] (the page's dI),
  * dWg, dWu [D, H], dWd [H, D]. Consumes the saved buffer: its G and U planes
  * hold dG and dU afterwards, and a second call on it computes garbage.
- * workspace may be NULL when swiglu_mlp_bwd_workspace_bytes() is 0. Outputs
- * must not overlap each other, the inputs, or the saved buffer. */
+ * workspace (>= swiglu_mlp_bwd_workspace_bytes() bytes, contents on entry
+ * irrelevant) may be NULL when that size is 0. Outputs and workspace must
+ * not overlap each other, the inputs, or the saved buffer. */
 int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu,
                    const void* Wd, void* saved, void* dX, void* dWg, void* dWu,
                    void* dWd, void* workspace, size_t workspace_bytes,

@@ -43,7 +43,10 @@ def test_size_queries():
     assert L.swiglu_mlp_saved_bytes(4096, 5632, 2) == 3 * 4096 * 5632 * 4
     assert L.swiglu_mlp_saved_bytes(10, 16, 9) == 0
     assert L.swiglu_mlp_infer_workspace_bytes(256, 4096, 11008, 0) == 256 * 11008 * 2
-    assert L.swiglu_mlp_bwd_workspace_bytes(65536, 4096, 11008, 0) == 0
+    assert L.swiglu_mlp_bwd_workspace_bytes(65536, 4096, 11008, 0) == 0   # tiles fill the GPU
+    assert L.swiglu_mlp_bwd_workspace_bytes(16384, 1024, 2816, 0) > 0     # split-K weight gradients
+    assert L.swiglu_mlp_bwd_workspace_bytes(16384, 1024, 2816, 2) == 0    # fp32 engine: no split
+    assert L.swiglu_mlp_bwd_workspace_bytes(512, 1024, 2816, 0) == 0      # small-T engine
 
 
 def test_infer_memory_matches_pages_table():
@@ -93,6 +96,16 @@ def test_host_validation_codes():
     assert call(args(dX=b[5] + 32)) == 5
     assert call(args(dWu=b[7] + 16)) == 5
     assert call(args(dWd=None)) == 1
+    # a split-K shape needs a workspace: missing, too small, overlapping
+    T, D, H = 16384, 1024, 2816
+    need = L.swiglu_mlp_bwd_workspace_bytes(T, D, H, 0)
+    callw = lambda a, ws, n: L.swiglu_mlp_bwd(*a[:10], ws, n, T, D, H, 0, None)
+    big = [BASE + (i << 34) for i in range(11)]
+    bargs = [big[i] for i in range(10)]
+    assert callw(bargs, None, 0) == 6
+    assert callw(bargs, big[10], need - 16) == 6
+    assert callw(bargs, big[10] + 8, need) == 4
+    assert callw(bargs, big[9] + 64, need) == 5
     # infer: workspace too small, then missing
     assert L.swiglu_mlp_infer(b[0], b[1], b[2], b[3], b[4], b[5], 16 * 128 * 2 - 2, 16, 64, 128, 0, None) == 6
     assert L.swiglu_mlp_infer(b[0], b[1], b[2], b[3], b[4], None, 0, 16, 64, 128, 0, None) == 6
