@@ -23,6 +23,7 @@
 // fp32 from the fp32 dA accumulator and the stored g and u, rounding dG and
 // dU once.
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -52,8 +53,11 @@ struct KArgs {
   int planes;      // PLAIN: number of (B source, output) planes (1 or 2)
   int group_m;     // M-tiles per group of the tile walk (tile_coords); 0 = 8
   int two_round;   // GATEUP: A = rnd(rnd(SiLU(g)) * u) instead of rnd(SiLU(g) * u)
-  float* P;        // PLAIN, split K: fp32 partials [ksplit][planes][M][N] (else nullptr)
-  int kchunk;      // PLAIN, split K: K stages per split (split = blockIdx.y)
+  float* P;        // PLAIN, split K: fp32 partial tiles, 256 x 256 each (else nullptr)
+  int kchunk;      // PLAIN, split K: K stages per piece
+  int n_full;      // weight-gradient launch: items (plane-major tiles) run whole
+  int ksplit;      // weight-gradient launch: pieces per split tile
+  int n_split;     // weight-gradient launch: tiles split over K (items n_full ..)
 };
 
 // Logistic function sigma(g) = 1 / (1 + exp(-g)) in fp32, from a stored gate
@@ -63,15 +67,18 @@ struct KArgs {
 // about 1 fp32 ulp, far below half an ulp of the 16-bit result, so the value
 // rounded to bf16/fp16 is the correctly rounded one except within ~1e-5
 // relative of a rounding tie (then 1 ulp away). For g <= -80 the reciprocal
-// nears the fp32 denormal range, where the hardware approximations flush;
-// those lanes take the IEEE form.
+// would near the fp32 denormal range, where the hardware approximations
+// flush; there sigma(g) equals e^g to fp32 precision (e^g < 2e-35), taken as
+// 2^(g log2 e + 64) * 2^-64: the exponential stays in the normal range and
+// the exact power-of-two scaling rounds once, into the denormals where the
+// value lies there. Both forms share one exponential and a select, with no
+// branch (the epilogues evaluate this for every element of a tile).
 __device__ __forceinline__ float sigmoid_ieee(float g) { return 1.0f / (1.0f + expf(-g)); }
 __device__ __forceinline__ float sigmoid_fast(float g) {
-  if (g > -80.0f) {
-    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
-    return __builtin_amdgcn_rcpf(1.0f + e);
-  }
-  return sigmoid_ieee(g);
+  const float x = g * 1.44269504088896341f;  // g log2 e
+  const bool lo = g <= -80.0f;
+  const float e = __builtin_amdgcn_exp2f(lo ? x + 64.0f : -x);
+  return lo ? e * 0x1p-64f : __builtin_amdgcn_rcpf(1.0f + e);
 }
 template <class E>
 __device__ __forceinline__ float sigmoid_f32(float g) {
@@ -89,6 +96,17 @@ __device__ __forceinline__ typename E::elem swiglu_a(float gf, float uf, int two
   const float silu = gf * sigmoid_f32<E>(gf);
   if (two_round) return E::from_f32(E::to_f32(E::from_f32(silu)) * uf);
   return E::from_f32(silu * uf);
+}
+
+// dG and dU from the fp32 dA and the stored gate and up values g, u, in fp32
+// (the caller rounds each once): dU = dA SiLU(g), dG = dA u SiLU'(g), with
+// SiLU'(g) = sigma (1 + g (1 - sigma)) = sigma + SiLU(g) (1 - sigma).
+template <class E>
+__device__ __forceinline__ void dswiglu(float da, float gf, float uf, float& dg, float& du) {
+  const float sg = sigmoid_f32<E>(gf);
+  const float silu = gf * sg;
+  du = da * silu;
+  dg = (da * uf) * fmaf(silu, 1.0f - sg, sg);
 }
 
 // Epilogue of one tile. acc[i][j][r] holds output
@@ -150,11 +168,10 @@ __device__ __forceinline__ void epilogue(const KArgs& g, char* C, f32x16_t (&acc
           V4 dg, du;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float da = acc[i][j][q * 4 + e];
-            float gf = E::to_f32(gv[e]), uf = E::to_f32(uv[e]);
-            float s = sigmoid_f32<E>(gf);
-            du[e] = E::from_f32(da * (gf * s));
-            dg[e] = E::from_f32(da * uf * (s * (1.0f + gf * (1.0f - s))));
+            float dgf, duf;
+            dswiglu<E>(acc[i][j][q * 4 + e], E::to_f32(gv[e]), E::to_f32(uv[e]), dgf, duf);
+            dg[e] = E::from_f32(dgf);
+            du[e] = E::from_f32(duf);
           }
           *(V4*)(g.c0 + off) = dg;
           *(V4*)(g.c1 + off) = du;
@@ -478,11 +495,10 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
             V4 dg, du;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float da = acc[i][j][q * 4 + e];
-              const float gf = E::to_f32(gv[e]), uf = E::to_f32(uv[e]);
-              const float sg = sigmoid_f32<E>(gf);
-              du[e] = E::from_f32(da * (gf * sg));
-              dg[e] = E::from_f32(da * uf * (sg * (1.0f + gf * (1.0f - sg))));
+              float dgf, duf;
+              dswiglu<E>(acc[i][j][q * 4 + e], E::to_f32(gv[e]), E::to_f32(uv[e]), dgf, duf);
+              dg[e] = E::from_f32(dgf);
+              du[e] = E::from_f32(duf);
             }
             pg.put4(r, c, dg);
             pu.put4(r, c, du);
@@ -514,7 +530,7 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
 // compiler wait for exactly the stage a read needs.
 template <class E, int AL, int BL, int KIND>
 __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, char* st2, char* st3, int bid,
-                                          int bz, int ks = 0) {
+                                          int bz, int ks = 0, int piece = -1) {
   using namespace ring;
   static_assert(E::kBytes == 2, "the ring pipeline is for bf16/fp16");
   // the wave index is uniform within a wave; readfirstlane lets the compiler
@@ -550,8 +566,9 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   da.init(A, m0, wave, lane);
   db.init(B, n0, wave, lane);
   const int nk1 = (A.k + BK - 1) / BK;
-  // split K (PLAIN with partials): stages [sb, sb + nk) of the K loop
-  const bool split = KIND == PLAIN && g.P != nullptr;
+  // split K (a piece of a weight-gradient tile): stages [sb, sb + nk) of
+  // the K loop, written as fp32 partial tile `piece`
+  const bool split = KIND == PLAIN && piece >= 0;
   const int sb = split ? ks * g.kchunk : 0;
   const int nk = (KIND == DX) ? 2 * nk1 : (split ? (nk1 - sb < g.kchunk ? nk1 - sb : g.kchunk) : nk1);
   char* st[4] = {st0, st1, st2, st3};
@@ -641,20 +658,21 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   }
   if constexpr (KIND == PLAIN) {
     if (split) {
-      // fp32 partial of this K split; lane holds 4 consecutive columns
-      float* P = g.P + ((int64_t)ks * g.planes + bz) * g.M * (int64_t)g.N;
+      // dense 256 x 256 fp32 partial tile (rows and columns past the
+      // matrix hold sums of zero operands; the reduction skips them); each
+      // lane holds 4 consecutive columns
+      float* P = g.P + (int64_t)piece * 65536;
       const int ml = lane & 31, nl = (lane >> 5) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + a_rows[i] + ml;
+        const int m = a_rows[i] + ml;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int n = n0 + b_rows[j] + q * 8 + nl;
-            if (m < g.M && n < g.N)
-              *(f32x4_t*)(P + (int64_t)m * g.N + n) =
-                  f32x4_t{acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
+            const int n = b_rows[j] + q * 8 + nl;
+            *(f32x4_t*)(P + m * 256 + n) =
+                f32x4_t{acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
           }
       }
       return;
@@ -810,9 +828,10 @@ constexpr int ring_variant() {
 }
 
 template <class E, int AL, int BL, int KIND>
-__device__ __forceinline__ void any_ring_tile(const KArgs& g, char* const (&R)[5], int bid, int bz, int ks) {
+__device__ __forceinline__ void any_ring_tile(const KArgs& g, char* const (&R)[5], int bid, int bz, int ks = 0,
+                                              int piece = -1) {
   if constexpr (ring_variant<AL, BL>() == 5) ring5_tile<E, AL, BL, KIND>(g, R, bid, bz);
-  else ring_tile<E, AL, BL, KIND>(g, R[0], R[1], R[2], R[3], bid, bz, ks);
+  else ring_tile<E, AL, BL, KIND>(g, R[0], R[1], R[2], R[3], bid, bz, ks, piece);
 }
 
 // Four 32 KiB LDS arrays, and a fifth when a five-array ring runs.
@@ -833,7 +852,28 @@ template <class E, int AL, int BL, int KIND, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ring_gemm(const KArgs g) {
   SWIGLU_RING_LDS((ring_variant<AL, BL>() == 5))
-  any_ring_tile<E, AL, BL, KIND>(g, R, blockIdx.x, blockIdx.z, blockIdx.y);
+  any_ring_tile<E, AL, BL, KIND>(g, R, blockIdx.x, blockIdx.z);
+}
+
+// Weight-gradient launch (PLAIN, K = T): items are tiles in plane-major
+// order. Items [0, n_full) run whole; each of the n_split items after them is
+// split into ksplit pieces over K (workgroup n_full + r * ksplit + s is piece
+// s of item n_full + r), which write fp32 partial tiles for
+// splitk_reduce_tiles. The split covers only the last, partly filled round of
+// tiles on the GPU's CUs.
+template <class E, int AL, int BL, int STAGE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+ring_wgrad(const KArgs g) {
+  SWIGLU_RING_LDS((ring_variant<AL, BL>() == 5))
+  const int nt = g.tiles_m * g.tiles_n;
+  const int b = blockIdx.x;
+  int item = b, ks = 0, piece = -1;
+  if (b >= g.n_full) {
+    piece = b - g.n_full;
+    item = g.n_full + piece / g.ksplit;
+    ks = piece % g.ksplit;
+  }
+  any_ring_tile<E, AL, BL, PLAIN>(g, R, item % nt, item / nt, ks, piece);
 }
 
 
@@ -1198,24 +1238,27 @@ __global__ void __launch_bounds__(256) stream_reduce(const KArgs g, const float*
   }
 }
 
-// Sum of the K-split partials of a PLAIN ring launch, in split order
-// (deterministic): C = rnd(sum over s of P[s]), for 1 or 2 output planes (c0,
-// c1). One thread per 4 consecutive outputs of a row.
+// Sum of the partial tiles of the split items of a weight-gradient launch, in
+// piece order (deterministic): C = rnd(sum over s of P[r * ksplit + s]) for
+// split item n_full + r, written to plane c0 or c1. One thread per 4
+// consecutive outputs of a tile row.
 template <class E>
-__global__ void __launch_bounds__(256) splitk_reduce(const float* P, int ksplit, int planes, int M, int N, char* c0,
-                                                     char* c1, int64_t ldc) {
+__global__ void __launch_bounds__(256) splitk_reduce_tiles(const KArgs g, const float* P) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per = (int64_t)M * (N / 4);
-  if (i >= per * planes) return;
-  const int z = (int)(i / per);
-  const int64_t r = i - z * per;
-  const int m = (int)(r / (N / 4)), n = (int)(r % (N / 4)) * 4;
+  if (i >= (int64_t)g.n_split * 16384) return;
+  const int r = (int)(i >> 14), rr = (int)(i >> 6) & 255, cq = (int)i & 63;
+  const int nt = g.tiles_m * g.tiles_n, item = g.n_full + r;
+  int tm, tn;
+  tile_coords(item % nt, g.tiles_m, g.tiles_n, g.group_m > 0 ? g.group_m : 8, tm, tn);
+  const int m = tm * 256 + rr, n = tn * 256 + cq * 4;
+  if (m >= g.M || n >= g.N) return;
+  const float* p = P + (int64_t)r * g.ksplit * 65536 + rr * 256 + cq * 4;
   f32x4_t sum = f32x4_t{};
-  for (int s = 0; s < ksplit; ++s) sum += *(const f32x4_t*)(P + (((int64_t)s * planes + z) * M + m) * N + n);
+  for (int s = 0; s < g.ksplit; ++s) sum += *(const f32x4_t*)(p + (int64_t)s * 65536);
   typename E::vec4 v;
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = E::from_f32(sum[e]);
-  *(typename E::vec4*)((z ? c1 : c0) + ((int64_t)m * ldc + n) * E::kBytes) = v;
+  *(typename E::vec4*)((item >= nt ? g.c1 : g.c0) + ((int64_t)m * g.ldc + n) * E::kBytes) = v;
 }
 
 // Fill kernel (used to clear weight gradients when T = 0 would otherwise
@@ -1286,6 +1329,27 @@ static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
 // T = 65536).
 constexpr int kRingGroupM = 2;
 
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Compute units of the current device (launch plans size work per CU);
+// cached per device, 256 when the runtime cannot say.
+static int dev_ncu() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int v = 0;
+    n = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Modelled time of one 256 x 256 ring tile with K values of K on one CU
+// (about 5 TFLOP/s per CU), used only to size launch plans.
+static inline double ring_tile_us(int64_t K) { return 2.0 * 256 * 256 * (double)K / 5.0e6; }
+
 template <class E, int AL, int BL, int KIND, int STAGE>
 static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
   a.group_m = kRingGroupM;
@@ -1297,58 +1361,71 @@ static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
-
-static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
-// K splits for a weight-gradient ring launch (K = T) with under half as many
-// output tiles as CUs: enough splits for about one workgroup per CU, each at
-// least 16 K stages. With 128 or more tiles, writing and adding the fp32
-// partials cost more than the idle CUs (measured at D = 2048, H = 5632 and at
-// H = 1376), so those run unsplit.
-static inline void splitk_plan(int tiles, int64_t K, int& splits, int& kchunk) {
+// Work split of a weight-gradient ring launch (K = T; nt tiles over all
+// planes). Whole rounds of tiles (one per CU) run unsplit. The remaining
+// rem = nt % ncu tiles would leave the last round partly idle, so each is
+// split into s pieces over K, s chosen by a model: ceil(rem s / ncu) rounds
+// of 1/s of a tile, plus writing and reading the fp32 partial tiles (256 KiB
+// each), plus the reduction launch. With no remainder, or no gain, nothing
+// is split.
+struct WgradPlan {
+  int n_full, n_split, ksplit, kchunk;
+};
+static WgradPlan wgrad_plan(int nt, int64_t K, int ncu) {
   const int nk = cdiv(K, ring::BK);
-  splits = 1;
-  kchunk = nk;
-  if (tiles >= 128) return;
-  int s = cdiv(256, tiles);
-  if (s > nk / 16) s = nk / 16;
-  if (s <= 1) return;
-  kchunk = cdiv(nk, s);
-  splits = cdiv(nk, kchunk);
+  WgradPlan p{nt, 0, 1, nk};
+  const int rem = nt % ncu;
+  if (rem == 0) return p;
+  const double tile = ring_tile_us(K);
+  double best = tile;
+  int bs = 1;
+  for (int s = 2; s <= 16 && nk / s >= 16; ++s) {
+    const double t = cdiv((int64_t)rem * s, ncu) * tile / s + (double)rem * s * 65536 * 4 * 2 / 4.0e6 + 5.0;
+    if (t < 0.97 * best) {
+      best = t;
+      bs = s;
+    }
+  }
+  if (bs == 1) return p;
+  p.n_full = nt - rem;
+  p.n_split = rem;
+  p.kchunk = cdiv(nk, bs);
+  p.ksplit = cdiv(nk, p.kchunk);
+  return p;
 }
 
-// Ring launch of a PLAIN stage, split over K when splitk_plan says so: fp32
-// partials into P, then splitk_reduce into the outputs; timed as one stage.
+// Weight-gradient ring launch (PLAIN, 1 or 2 planes) following wgrad_plan:
+// whole tiles write the outputs; split tiles write fp32 partials into P,
+// then splitk_reduce_tiles adds them; timed as one stage.
 template <class E, int AL, int BL, int STAGE>
-static int launch_ring_splitk(KArgs a, int grid_z, float* P, hipStream_t stream) {
-  int splits, kchunk;
-  splitk_plan(a.tiles_m * a.tiles_n * grid_z, a.a0.k, splits, kchunk);
-  if (splits <= 1) {
-    a.P = nullptr;
-    return launch_ring<E, AL, BL, PLAIN, STAGE>(a, grid_z, stream);
-  }
-  const int nb = a.tiles_m * a.tiles_n;
+static int launch_ring_wgrad(KArgs a, int grid_z, float* P, hipStream_t stream) {
+  const int nt = a.tiles_m * a.tiles_n;
+  if (nt <= 0) return SWIGLU_OK;
+  const WgradPlan pl = wgrad_plan(nt * grid_z, a.a0.k, dev_ncu());
   a.planes = grid_z;
   a.group_m = kRingGroupM;
-  a.P = P;
-  a.kchunk = kchunk;
+  a.P = pl.n_split ? P : nullptr;
+  a.kchunk = pl.kchunk;
+  a.n_full = pl.n_full;
+  a.ksplit = pl.ksplit;
+  a.n_split = pl.n_split;
   StageScope scope(STAGE, stream);
-  hipLaunchKernelGGL((ring_gemm<E, AL, BL, PLAIN, STAGE>), dim3(nb, splits, grid_z), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((ring_wgrad<E, AL, BL, STAGE>), dim3(pl.n_full + pl.n_split * pl.ksplit), dim3(256), 0, stream,
+                     a);
   if (hipGetLastError() != hipSuccess) return SWIGLU_ERR_LAUNCH;
-  const int64_t nq = (int64_t)grid_z * a.M * (a.N / 4);
-  hipLaunchKernelGGL((splitk_reduce<E>), dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream, (const float*)P,
-                     splits, grid_z, a.M, a.N, a.c0, a.c1, a.ldc);
+  if (pl.n_split == 0) return SWIGLU_OK;
+  hipLaunchKernelGGL((splitk_reduce_tiles<E>), dim3(pl.n_split * 64), dim3(256), 0, stream, a, (const float*)P);
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
-// fp32 partial bytes of the split weight-gradient launches (bf16/fp16, T >
-// 512): the larger of dWd ([H, D]) and [dWg | dWu] (2 x [D, H]).
+// fp32 partial bytes of the weight-gradient launches (bf16/fp16, T > 512):
+// the larger of dWd ([H, D]) and [dWg | dWu] (2 x [D, H]).
 static inline size_t splitk_bytes(int64_t T, int64_t D, int64_t H) {
-  int sd, sg, kc;
-  splitk_plan(cdiv(H, 256) * cdiv(D, 256), T, sd, kc);
-  splitk_plan(cdiv(D, 256) * cdiv(H, 256) * 2, T, sg, kc);
-  const size_t pd = sd > 1 ? (size_t)sd * H * D * 4 : 0, pg = sg > 1 ? (size_t)sg * 2 * D * H * 4 : 0;
-  return pd > pg ? pd : pg;
+  const int ncu = dev_ncu();
+  const WgradPlan pd = wgrad_plan(cdiv(H, 256) * cdiv(D, 256), T, ncu);
+  const WgradPlan pg = wgrad_plan(cdiv(D, 256) * cdiv(H, 256) * 2, T, ncu);
+  const size_t bd = (size_t)pd.n_split * pd.ksplit * 65536 * 4, bg = (size_t)pg.n_split * pg.ksplit * 65536 * 4;
+  return bd > bg ? bd : bg;
 }
 
 // Few-token launch: one workgroup per 16 output columns.
@@ -1576,8 +1653,8 @@ struct Path {
       // short-K stages with the long-K weight gradients on the ring engine
       int rc;
       if ((rc = launch_ring<E, KC, KC, DSWIGLU, 2>(dgu, 1, s))) return rc;
-      if ((rc = launch_ring_splitk<E, MC, MC, 3>(dwd, 1, P, s))) return rc;
-      if ((rc = launch_ring_splitk<E, MC, MC, 4>(dwgu, 2, P, s))) return rc;
+      if ((rc = launch_ring_wgrad<E, MC, MC, 3>(dwd, 1, P, s))) return rc;
+      if ((rc = launch_ring_wgrad<E, MC, MC, 4>(dwgu, 2, P, s))) return rc;
       return launch_ring<E, KC, KC, DX, 5>(dx, 1, s);
     } else {
       int rc = launch_pair<E, MC, MC, PLAIN, KC, KC, DSWIGLU, 8>(dwd, dgu, s);

@@ -97,11 +97,13 @@ size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
  * about 34 MB at D = 4096, H = 11008, T = 128. 0 on bad args. */
 size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
 
-/* Bytes of the backward workspace: fp32 partial sums of the weight-gradient
- * GEMMs (K = T) when they have under half as many output tiles as the GPU
- * has CUs and are split over K (bf16/fp16, T > 512: for example D = 1024,
- * H = 2816, or H = 1376 at D = 4096). 0 when no split is needed, as at
- * D = 4096, H = 11008, and for fp32. 0 on bad args. */
+/* Bytes of the backward workspace: fp32 partial tiles (256 x 256, 256 KiB
+ * each) of the weight-gradient GEMMs (K = T; bf16/fp16, T > 512). Their
+ * 256 x 256 output tiles run whole in rounds of one per CU of the current
+ * device; the tiles of a partly filled last round are split over K when
+ * that is modelled to be faster (for example D = 4096, H = 11008: 176 tiles
+ * of dWd in 4 pieces, 176 MiB). 0 when no tile is split (whole
+ * rounds, as at D = 4096, H = 8192) and for fp32. 0 on bad args. */
 size_t swiglu_mlp_bwd_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
 
 /* Forward for training. Reads X, Wg, Wu, Wd; writes Y [T, D] and the saved

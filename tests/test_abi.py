@@ -43,7 +43,12 @@ def test_size_queries():
     assert L.swiglu_mlp_saved_bytes(4096, 5632, 2) == 3 * 4096 * 5632 * 4
     assert L.swiglu_mlp_saved_bytes(10, 16, 9) == 0
     assert L.swiglu_mlp_infer_workspace_bytes(256, 4096, 11008, 0) == 256 * 11008 * 2
-    assert L.swiglu_mlp_bwd_workspace_bytes(65536, 4096, 11008, 0) == 0   # tiles fill the GPU
+    # weight gradients: whole rounds of 256 tiles run unsplit; the tiles of a
+    # partly filled last round are split over K into fp32 partial tiles
+    # (256 KiB each). D=4096, H=11008: dWd has 43 x 16 = 688 tiles = 2 rounds
+    # + 176, split 4 ways; [dWg | dWu] has 1376 = 5 rounds + 96, split 5 ways.
+    assert L.swiglu_mlp_bwd_workspace_bytes(65536, 4096, 11008, 0) == 176 * 4 * 256 * 256 * 4
+    assert L.swiglu_mlp_bwd_workspace_bytes(65536, 4096, 8192, 0) == 0    # 512 and 1024 tiles: whole rounds
     assert L.swiglu_mlp_bwd_workspace_bytes(16384, 1024, 2816, 0) > 0     # split-K weight gradients
     assert L.swiglu_mlp_bwd_workspace_bytes(16384, 1024, 2816, 2) == 0    # fp32 engine: no split
     assert L.swiglu_mlp_bwd_workspace_bytes(512, 1024, 2816, 0) == 0      # small-T engine
