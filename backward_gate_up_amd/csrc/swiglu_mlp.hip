@@ -472,40 +472,52 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
       pu.store(g.c2, g.ldc, r0, c0, g.M, g.N, 128, lane);
     }
   } else if constexpr (KIND == DSWIGLU) {
-    // wave block: 128 rows x 128 hidden units, in two halves of 64 rows; the
-    // G and U blocks are loaded into LDS, turned into dG and dU in place
-    // (the same (t, h) block of this tile only), and stored back.
-    WaveBlock<E, 128> pg{wbuf}, pu{wbuf + 16384};
+    // wave block: 128 rows x 128 hidden units, in four quarters of 32 rows
+    // (one MFMA row block each). The G and U rows of a quarter are loaded
+    // into LDS, turned into dG and dU in place (this tile's own (t, h) block
+    // only) and stored back. Two LDS slots of 16 KiB: the loads of quarter
+    // q + 1 are in flight while quarter q is computed and stored, and those
+    // of q + 2 reuse q's slot once its stores have read it. vmcnt counts
+    // this wave's loads and stores in issue order: [loads 0] [loads 1]
+    // [stores 0] [loads 2] [stores 1] [loads 3] [stores 2] ... A quarter's
+    // stores may be fewer than 16 instructions (rows past M are skipped), so
+    // each wait lets only the 16 loads issued last stay outstanding.
     const int64_t plane_bytes = (int64_t)g.M * g.ldc * 2;
+    const int c0 = n0 + wn * 128;
+    auto issue = [&](int q) {
+      char* slot = wbuf + (q & 1) * 16384;
+      const int r0 = m0 + wm * 128 + q * 32;
+      WaveBlock<E, 128>{slot}.load(g.c0, g.ldc, plane_bytes, r0, c0, 32, lane);
+      WaveBlock<E, 128>{slot + 8192}.load(g.c1, g.ldc, plane_bytes, r0, c0, 32, lane);
+    };
+    issue(0);
+    issue(1);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int r0 = m0 + wm * 128 + hf * 64, c0 = n0 + wn * 128;
-      pg.load(g.c0, g.ldc, plane_bytes, r0, c0, 64, lane);
-      pu.load(g.c1, g.ldc, plane_bytes, r0, c0, 64, lane);
-      ring::wait_vmcnt<0>();
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) ring::wait_vmcnt<16>();  // loads of q + 1 may stay in flight
+      else ring::wait_vmcnt<0>();
+      WaveBlock<E, 128> pg{wbuf + (q & 1) * 16384}, pu{wbuf + (q & 1) * 16384 + 8192};
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = hf * 2 + ii;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int qq = 0; qq < 4; ++qq) {
+          const int r = ml, c = j * 32 + qq * 8 + nl;
+          const V4 gv = pg.get4(r, c), uv = pu.get4(r, c);
+          V4 dg, du;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = ii * 32 + ml, c = j * 32 + q * 8 + nl;
-            const V4 gv = pg.get4(r, c), uv = pu.get4(r, c);
-            V4 dg, du;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float dgf, duf;
-              dswiglu<E>(acc[i][j][q * 4 + e], E::to_f32(gv[e]), E::to_f32(uv[e]), dgf, duf);
-              dg[e] = E::from_f32(dgf);
-              du[e] = E::from_f32(duf);
-            }
-            pg.put4(r, c, dg);
-            pu.put4(r, c, du);
+          for (int e = 0; e < 4; ++e) {
+            float dgf, duf;
+            dswiglu<E>(acc[q][j][qq * 4 + e], E::to_f32(gv[e]), E::to_f32(uv[e]), dgf, duf);
+            dg[e] = E::from_f32(dgf);
+            du[e] = E::from_f32(duf);
           }
-      }
-      pg.store(g.c0, g.ldc, r0, c0, g.M, g.N, 64, lane);
-      pu.store(g.c1, g.ldc, r0, c0, g.M, g.N, 64, lane);
+          pg.put4(r, c, dg);
+          pu.put4(r, c, du);
+        }
+      const int r0 = m0 + wm * 128 + q * 32;
+      pg.store(g.c0, g.ldc, r0, c0, g.M, g.N, 32, lane);
+      pu.store(g.c1, g.ldc, r0, c0, g.M, g.N, 32, lane);
+      if (q + 2 < 4) issue(q + 2);
     }
   } else {
     // PLAIN / DX: 128 x 128 block of C
@@ -1323,11 +1335,15 @@ static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
-// Tile walk of the ring kernels: each XCD runs 2 M-tiles x 16 N-tiles at a
-// time, so that many concurrent tiles share the rows of the large T-indexed
-// operand (measured best of 1, 2, 4, 8, 16 at D = 4096, H = 11008,
-// T = 65536).
-constexpr int kRingGroupM = 2;
+// Tile walk of the ring kernels (tile_coords): each XCD runs group_m M-tiles
+// x (32 / group_m) N-tiles at a time, so that its concurrent tiles share
+// operand rows through its L2. Per stage, measured over 2, 4 and 8 at
+// D = 4096, H = 11008, T = 65536 (the differences are 0.5-2.5 %): 2 for
+// gate/up, down and dI; 4 for the weight gradients; 8 for dA + dSwiGLU.
+template <int KIND, int STAGE>
+constexpr int ring_group_m() {
+  return KIND == DSWIGLU ? 8 : (STAGE == 3 || STAGE == 4) ? 4 : 2;
+}
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -1352,7 +1368,7 @@ static inline double ring_tile_us(int64_t K) { return 2.0 * 256 * 256 * (double)
 
 template <class E, int AL, int BL, int KIND, int STAGE>
 static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
-  a.group_m = kRingGroupM;
+  a.group_m = ring_group_m<KIND, STAGE>();
   const int nb = a.tiles_m * a.tiles_n;
   a.planes = grid_z;
   if (nb <= 0) return SWIGLU_OK;
@@ -1403,7 +1419,7 @@ static int launch_ring_wgrad(KArgs a, int grid_z, float* P, hipStream_t stream) 
   if (nt <= 0) return SWIGLU_OK;
   const WgradPlan pl = wgrad_plan(nt * grid_z, a.a0.k, dev_ncu());
   a.planes = grid_z;
-  a.group_m = kRingGroupM;
+  a.group_m = ring_group_m<PLAIN, STAGE>();
   a.P = pl.n_split ? P : nullptr;
   a.kchunk = pl.kchunk;
   a.n_full = pl.n_full;
