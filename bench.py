@@ -310,7 +310,7 @@ def ingest_traffic(fetch_csv, write_csv, copy_mib, command):
         out[f"{key}_factor"] = round(factor, 4)
         per_stage = defaultdict(list)
         for k, v in vals.items():
-            m = re.search(r"(mlp_gemm|mlp_gemm_pair|ring_gemm)<.*,\s*(\d+)>\(", names[k])
+            m = re.search(r"(mlp_gemm|mlp_gemm_pair|ring_gemm|ring_wgrad)<.*,\s*(\d+)>\(", names[k])
             if m:
                 per_stage[STAGE_NAMES[int(m.group(2))]].append(v * factor)
         res[key] = {st: sum(v) / len(v) for st, v in per_stage.items()}
