@@ -80,6 +80,10 @@ __device__ __forceinline__ float sigmoid_fast(float g) {
   const float e = __builtin_amdgcn_exp2f(lo ? x + 64.0f : -x);
   return lo ? e * 0x1p-64f : __builtin_amdgcn_rcpf(1.0f + e);
 }
+// The fast form for g > -80 (and g = -Inf, NaN) only.
+__device__ __forceinline__ float sigmoid_fast_hi(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+}
 template <class E>
 __device__ __forceinline__ float sigmoid_f32(float g) {
   if constexpr (E::kBytes == 4) return sigmoid_ieee(g);
@@ -98,6 +102,36 @@ __device__ __forceinline__ typename E::elem swiglu_a(float gf, float uf, int two
   return E::from_f32(silu * uf);
 }
 
+// sigma of four gate values of one lane. 16-bit storage: the branch-free fast
+// form, except that the g <= -80 range is taken only when some lane of the
+// wave has such a value among its four (a wave-uniform branch, almost never
+// taken), so the common case skips that range's instructions.
+template <class E>
+__device__ __forceinline__ void sigmoid4(const float (&g)[4], float (&sg)[4]) {
+  if constexpr (E::kBytes == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sg[e] = sigmoid_ieee(g[e]);
+  } else {
+    const float gmin = fminf(fminf(g[0], g[1]), fminf(g[2], g[3]));
+    if (__any(gmin <= -80.0f)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sg[e] = sigmoid_fast(g[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sg[e] = sigmoid_fast_hi(g[e]);
+    }
+  }
+}
+
+// A from g, sigma(g) and u: the one-round (TWO = false) or two-round program
+// of swiglu_a, with the program fixed at compile time.
+template <class E, bool TWO>
+__device__ __forceinline__ typename E::elem swiglu_a_s(float gf, float sg, float uf) {
+  const float silu = gf * sg;
+  if constexpr (TWO) return E::from_f32(E::to_f32(E::from_f32(silu)) * uf);
+  else return E::from_f32(silu * uf);
+}
+
 // dG and dU from the fp32 dA and the stored gate and up values g, u, in fp32
 // (the caller rounds each once): dU = dA SiLU(g), dG = dA u SiLU'(g), with
 // SiLU'(g) = sigma (1 + g (1 - sigma)) = sigma + SiLU(g) (1 - sigma).
@@ -107,6 +141,19 @@ __device__ __forceinline__ void dswiglu(float da, float gf, float uf, float& dg,
   const float silu = gf * sg;
   du = da * silu;
   dg = (da * uf) * fmaf(silu, 1.0f - sg, sg);
+}
+// The same for four elements of one lane, with sigmoid4.
+template <class E>
+__device__ __forceinline__ void dswiglu4(const float (&da)[4], const float (&gf)[4], const float (&uf)[4],
+                                         float (&dg)[4], float (&du)[4]) {
+  float sg[4];
+  sigmoid4<E>(gf, sg);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float silu = gf[e] * sg[e];
+    du[e] = da[e] * silu;
+    dg[e] = (da[e] * uf[e]) * fmaf(silu, 1.0f - sg[e], sg[e]);
+  }
 }
 
 // Epilogue of one tile. acc[i][j][r] holds output
@@ -436,24 +483,31 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
     // wave block: 128 rows (t) x 64 hidden units, planes A, G, U
     WaveBlock<E, 64> pa{wbuf}, pg{wbuf + 16384};
     const int r0 = m0 + wm * 128, c0 = n0 + wn * 64;
+    // A and G into LDS; the program (one- or two-round) is fixed per launch
+    auto stage_ag = [&](auto two) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          V4 gv, av;
+          for (int q = 0; q < 4; ++q) {
+            V4 gv, av;
+            float gf[4], uf[4], sg[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            typename E::elem gs = E::from_f32(acc[i][j][q * 4 + e]);
-            typename E::elem us = E::from_f32(acc[i][j + 2][q * 4 + e]);
-            const float gf = E::to_f32(gs), uf = E::to_f32(us);
-            gv[e] = gs;
-            av[e] = swiglu_a<E>(gf, uf, g.two_round);
+            for (int e = 0; e < 4; ++e) {
+              gv[e] = E::from_f32(acc[i][j][q * 4 + e]);
+              gf[e] = E::to_f32(gv[e]);
+              uf[e] = E::to_f32(E::from_f32(acc[i][j + 2][q * 4 + e]));
+            }
+            sigmoid4<E>(gf, sg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = swiglu_a_s<E, decltype(two)::value>(gf[e], sg[e], uf[e]);
+            pa.put4(i * 32 + ml, j * 32 + q * 8 + nl, av);
+            pg.put4(i * 32 + ml, j * 32 + q * 8 + nl, gv);
           }
-          pa.put4(i * 32 + ml, j * 32 + q * 8 + nl, av);
-          pg.put4(i * 32 + ml, j * 32 + q * 8 + nl, gv);
-        }
+    };
+    if (g.two_round) stage_ag(std::true_type{});
+    else stage_ag(std::false_type{});
     pa.store(g.c0, g.ldc, r0, c0, g.M, g.N, 128, lane);
     if (g.store_gu) {
       pg.store(g.c1, g.ldc, r0, c0, g.M, g.N, 128, lane);
@@ -504,12 +558,18 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
           const int r = ml, c = j * 32 + qq * 8 + nl;
           const V4 gv = pg.get4(r, c), uv = pu.get4(r, c);
           V4 dg, du;
+          float da[4], gf[4], uf[4], dgf[4], duf[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float dgf, duf;
-            dswiglu<E>(acc[q][j][qq * 4 + e], E::to_f32(gv[e]), E::to_f32(uv[e]), dgf, duf);
-            dg[e] = E::from_f32(dgf);
-            du[e] = E::from_f32(duf);
+            da[e] = acc[q][j][qq * 4 + e];
+            gf[e] = E::to_f32(gv[e]);
+            uf[e] = E::to_f32(uv[e]);
+          }
+          dswiglu4<E>(da, gf, uf, dgf, duf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dg[e] = E::from_f32(dgf[e]);
+            du[e] = E::from_f32(duf[e]);
           }
           pg.put4(r, c, dg);
           pu.put4(r, c, du);
