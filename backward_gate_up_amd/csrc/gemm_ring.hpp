@@ -35,10 +35,6 @@ namespace swiglu {
 namespace ring {
 
 constexpr int BK = 32;               // K per stage of the four-stage ring
-#ifndef SWIGLU_RING_STAGES
-#define SWIGLU_RING_STAGES 4
-#endif
-constexpr int NST = SWIGLU_RING_STAGES;  // LDS stages (loads run NST - 1 stages ahead)
 constexpr int OPB = 256 * BK * 2;    // one operand tile per stage: 16 KiB
 constexpr int STAGE = 2 * OPB;       // 32 KiB
 constexpr int L = 8;                 // loads per wave per stage (4 for A, 4 for B)

@@ -119,14 +119,16 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // assembly, the compiler neither sees the LDS write nor waits for it: the
 // caller waits (s_waitcnt vmcnt counts this wave's loads in issue order) and
 // publishes with a barrier. The memory clobber keeps other memory accesses
-// on their side of it.
+// on their side of it. The LDS address goes in through an {m0} operand, so
+// the compiler itself writes M0 and knows that it changed; the s_nop is the
+// wait state between that write and the load that reads it.
 __device__ __forceinline__ void dma16(uint32_t lds, i32x4_t rs, uint32_t voff, uint32_t soff) {
   // wave-uniform by contract; readfirstlane keeps them in scalar registers
   // where the compiler could not prove it
   lds = __builtin_amdgcn_readfirstlane(lds);
   soff = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds), "v"(voff), "s"(rs), "s"(soff)
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds)
                : "memory");
 }
 

@@ -14,8 +14,11 @@
  * Shapes and layouts. All matrices are dense and row-major (last index
  * contiguous): X, Y, dY, dX are [T, D]; Wg, Wu, dWg, dWu are [D, H];
  * Wd, dWd are [H, D]. All tensors of one call share one dtype. T >= 0 is any
- * value; D and H must be positive multiples of 8. Every pointer must be
- * 16-byte aligned; pointers to buffers of zero bytes (T = 0) may be NULL.
+ * value below 2^31; D and H must be positive multiples of 8, at most 4194296
+ * for bf16/fp16 and 2097144 for fp32 (the kernels address a 256-row tile of
+ * any operand with 32-bit byte offsets), and every launch's tile count must
+ * fit in 32 bits. Every pointer must be 16-byte aligned; pointers to buffers
+ * of zero bytes (T = 0) may be NULL.
  *
  * Numerics. bf16/fp16 storage with fp32 accumulation; every stored value is
  * rounded once (round to nearest even) from fp32. The SwiGLU epilogue is the
@@ -64,7 +67,7 @@ typedef enum {
 typedef enum {
   SWIGLU_OK = 0,
   SWIGLU_ERR_NULL = 1,      /* a required pointer is NULL */
-  SWIGLU_ERR_SHAPE = 2,     /* T < 0, D or H <= 0 or not a multiple of 8, or a size overflows */
+  SWIGLU_ERR_SHAPE = 2,     /* T < 0, D or H <= 0, not a multiple of 8 or above the limit, or a size overflows */
   SWIGLU_ERR_DTYPE = 3,     /* unknown dtype */
   SWIGLU_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
   SWIGLU_ERR_ALIAS = 5,     /* an output overlaps an input or another output */

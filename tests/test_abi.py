@@ -141,3 +141,29 @@ def test_unknown_flags_rejected_before_anything_else():
     assert L.swiglu_mlp_fwd_ex(*b[:6], 16, 64, 128, 7, 2, None) == 3
     assert L.swiglu_mlp_fwd_ex(b[0], b[1], b[2], b[3], b[0] + 64, b[5], 16, 64, 128, 0, 1, None) == 5
     assert L.swiglu_mlp_infer_ex(*b[:5], None, 0, 16, 64, 128, 0, 1, None) == 6
+
+
+def test_shape_limits_of_32_bit_lane_offsets():
+    """D and H are the leading dimensions of every operand. A tile spans 256
+    rows, so its lane offsets reach 256 * ld * elt_bytes, which must stay
+    below 2^31: D, H <= 4194296 for bf16/fp16 and <= 2097144 for fp32
+    (multiples of 8). Just inside the limit the call gets past the shape
+    check and fails on the misaligned Wd; just outside it returns
+    SWIGLU_ERR_SHAPE. Nothing is launched either way."""
+    L = _lib()
+    far = [1 << 44, 2 << 44, 3 << 44, 4 << 44, 5 << 44, 6 << 44]
+    for dt, lim in ((0, 4194296), (1, 4194296), (2, 2097144)):
+        for which in ("D", "H"):
+            def call(v, misalign=True):
+                D, H = (v, 64) if which == "D" else (64, v)
+                b = list(far)
+                if misalign:
+                    b[3] += 8
+                return L.swiglu_mlp_fwd(*b, 16, D, H, dt, None)
+            assert call(lim) == 4, (dt, which)            # past the shape check
+            assert call(lim + 8) == 2, (dt, which)        # SWIGLU_ERR_SHAPE
+            assert L.swiglu_mlp_infer(*far[:5], far[5], 1 << 40, 16, *((lim + 8, 64) if which == "D" else (64, lim + 8)),
+                                      dt, None) == 2
+    # the tile count of a launch must fit in int32
+    assert L.swiglu_mlp_fwd(*far[:3], far[3] + 8, *far[4:], (1 << 31) - 1, 8, 8, 0, None) == 4
+    assert L.swiglu_mlp_fwd(*far, (1 << 31) - 1, 4194296, 64, 0, None) == 2

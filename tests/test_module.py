@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 from synth import make_inputs
-from tests._util import TOL, banner, f64, nl2
+from tests._util import TOL, assert_local, banner, f64, fmt_local
 
 pytestmark = pytest.mark.gpu
 
@@ -45,13 +45,11 @@ def test_module_grads_vs_oracle(mlp, B, S, D, H, dt):
     (y.float() * dy.float()).sum().backward()
     f = {k: v.float().numpy() for k, v in inp.items()}
     ref = O.bwd(f["dY"], f["X"], f["Wg"], f["Wu"], f["Wd"])
-    errs = {"Y": nl2(f64(y.reshape(B * S, D)), O.fwd(f["X"], f["Wg"], f["Wu"], f["Wd"])["Y"]),
-            "dI": nl2(f64(x.grad.reshape(B * S, D)), ref["dI"]),
-            "dWg": nl2(f64(mod.w_gate.grad), ref["dWg"]), "dWu": nl2(f64(mod.w_up.grad), ref["dWu"]),
-            "dWd": nl2(f64(mod.w_down.grad), ref["dWd"])}
-    banner(" ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, v in errs.items():
-        assert v <= TOL[fmt], (k, v)
+    ref["Y"] = O.fwd(f["X"], f["Wg"], f["Wu"], f["Wd"])["Y"]
+    got = {"Y": y.reshape(B * S, D), "dI": x.grad.reshape(B * S, D), "dWg": mod.w_gate.grad,
+           "dWu": mod.w_up.grad, "dWd": mod.w_down.grad}
+    for k, v in got.items():
+        banner(f"{k} {fmt_local(assert_local(f64(v), ref[k], TOL[fmt], ('module', k)))}")
     with torch.no_grad():
         y_ng = mod(x)
     torch.cuda.synchronize()

@@ -1,11 +1,17 @@
 """Parity of the HIP path with the fp64 oracle (GPU).
 
 Bounds: normalized L2 <= 1e-2 for bf16/fp16 outputs and gradients, <= 1e-5
-in fp32 mode; the forward SwiGLU epilogue within 1 ulp of the correctly
-rounded SiLU(g)*u of the GPU's own stored g, u. Small shapes exercise ragged
-tails in every dimension; the pages' training shapes run in full; the
-largest one (T = 65536, D = 4096, H = 11008) is checked on sampled rows and
-hidden units in the same launch configuration the benchmark times.
+in fp32 mode, over the whole tensor and also over every row, every 32 x 32
+block and every 256 x 256 tile (tests/_util.py, local_errors), so that one
+wrong row, matrix-core block or split-K tile cannot hide in the global
+figure; the forward SwiGLU epilogue within 1 ulp of the correctly rounded
+SiLU(g)*u of the GPU's own stored g, u. Small shapes exercise ragged tails in
+every dimension; the pages' training shapes run in full; the largest one
+(T = 65536, D = 4096, H = 11008) is checked in the same launch configuration
+the benchmark times, on one row in every 32-row block and one hidden unit in
+every 32-unit block, which touches every 32 x 32 block row and every tile of
+each output, including every weight-gradient tile that the library splits
+over K.
 """
 
 import numpy as np
@@ -14,7 +20,7 @@ import torch
 
 import oracle as O
 from synth import WORKLOADS, make_inputs, workload_inputs
-from tests._util import TOL, banner, f64, nl2, run_train, to_dev
+from tests._util import SAMPLED, TOL, assert_local, banner, f64, fmt_local, nl2, run_train, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -39,13 +45,11 @@ def _check_full(mlp, inp, fmt, label, check_planes=True):
     if not check_planes:
         ref["Y"] = O.fwd(f["X"], f["Wg"], f["Wu"], f["Wd"])["Y"]
     tol = TOL[fmt]
-    errs = {k: nl2(f64(out[k]), ref[k]) for k in ("Y", "dI", "dWg", "dWu", "dWd")}
-    if check_planes:
-        for k in ("G", "U", "dG", "dU"):
-            errs[k] = nl2(f64(out[k]), ref[k])
-    banner(f"{label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, v in errs.items():
-        assert v <= tol, (label, k, v)
+    keys = ["Y", "dI", "dWg", "dWu", "dWd"] + (["G", "U", "dG", "dU"] if check_planes else [])
+    errs = {}
+    for k in keys:
+        errs[k] = assert_local(f64(out[k]), ref[k], tol, (label, k))
+        banner(f"{label}: {k} {fmt_local(errs[k])}")
     # the backward leaves the A plane untouched
     assert torch.equal(out["A"], out["A_after"])
     # forward epilogue: A within 1 ulp of rnd(SiLU(g) u) from the stored g, u
@@ -113,38 +117,68 @@ def test_fp32_and_fp16_ragged(mlp):
         _check_full(mlp, inp, fmt, f"{fmt} T=333 D=136 H=264")
 
 
+def _one_per_block(n, rng, b=32):
+    """One index in every b-wide block of range(n) (the last block may be
+    partial), drawn at random within the block."""
+    starts = np.arange(0, n, b)
+    return starts + rng.integers(0, np.minimum(b, n - starts))
+
+
+def _tiles_touched(idx, n, t=256):
+    return set((np.asarray(idx) // t).tolist()) == set(range((n + t - 1) // t))
+
+
+def _check_sampled(label, got, ref, tol=1e-2):
+    """Sampled rows (or transposed sampled columns) against the oracle: each
+    sampled line, and each 32- and 256-element segment of it (the footprint
+    of a matrix-core block and of a tile), within tol."""
+    e = assert_local(got, ref, tol, label, **SAMPLED)
+    banner(f"{label} {fmt_local(e)}")
+
+
 def test_headline_T65536_sampled(mlp):
-    """D=4096, H=11008, T=65536: sampled rows of Y and dI, sampled hidden
-    units for dWg, dWu (columns) and dWd (rows), plus the saved planes on the
-    sampled rows."""
+    """D=4096, H=11008, T=65536 through the same calls the benchmark times.
+    Rows: one in every 32-row block (2048 rows) of Y, dI and of the saved
+    planes G, U (after fwd) and dG, dU (after bwd). Hidden units: one in every
+    32-unit block (344 units) for dWg and dWu (columns) and dWd (rows). Every
+    256 x 256 tile of every output is touched, so every tile of dWd and of
+    [dWg | dWu] that the library splits over K (the 176 x 4 and 96 x 5 pieces
+    of its workspace) is checked too."""
+    T, D, H = 65536, 4096, 11008
     banner("T=65536: inputs")
     inp = workload_inputs("mlp_4096x11008_T65536")
     g = to_dev(inp)
+    rng = np.random.default_rng(65536)
+    rows = _one_per_block(T, rng)
+    hs = _one_per_block(H, rng)
+    assert _tiles_touched(rows, T) and _tiles_touched(hs, H)
+    assert mlp.bwd_workspace_bytes(T, D, H) == (176 * 4) * 256 * 256 * 4
     banner("T=65536: GPU fwd+bwd")
     y, saved = mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"])
-    rows = np.array([0, 1, 255, 256, 4097, 33333, 65279, 65535])
-    G_s = saved[1][rows].clone()
-    U_s = saved[2][rows].clone()
-    A_s = saved[0][rows].clone()
+    ridx = torch.as_tensor(rows, device="cuda")
+    A_s, G_s, U_s = (saved[i].index_select(0, ridx) for i in (0, 1, 2))
     dx, dwg, dwu, dwd = mlp.bwd(g["dY"], g["X"], g["Wg"], g["Wu"], g["Wd"], saved)
+    dG_s, dU_s = (saved[i].index_select(0, ridx) for i in (1, 2))
+    hidx = torch.as_tensor(hs, device="cuda")
+    got = {"Y": y.index_select(0, ridx), "dI": dx.index_select(0, ridx), "G": G_s, "U": U_s, "dG": dG_s,
+           "dU": dU_s, "dWg": dwg.index_select(1, hidx).t(), "dWu": dwu.index_select(1, hidx).t(),
+           "dWd": dwd.index_select(0, hidx)}
+    got = {k: f64(v) for k, v in got.items()}
+    a_s = f64(A_s)
     torch.cuda.synchronize()
-    del g
+    del g, y, saved, dx, dwg, dwu, dwd
     f = _np(inp)
     banner("T=65536: oracle rows")
     r = O.rows(rows, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
-    e = {"Y": nl2(f64(y[rows]), r["Y"]), "dI": nl2(f64(dx[rows]), r["dI"]),
-         "G": nl2(f64(G_s), r["G"]), "U": nl2(f64(U_s), r["U"])}
-    a_ref = O.round_to(O.epilogue_fwd(f64(G_s), f64(U_s)), "bf16")
-    assert int(O.ulp_distance(f64(A_s), a_ref, "bf16").max()) <= 1
+    a_ref = O.round_to(O.epilogue_fwd(got["G"], got["U"]), "bf16")
+    assert int(O.ulp_distance(a_s, a_ref, "bf16").max()) <= 1
+    for k in ("Y", "dI", "G", "U", "dG", "dU"):
+        _check_sampled(f"T=65536 {k}", got[k], r[k])
     banner("T=65536: oracle hidden units")
-    hs = np.array([0, 1, 127, 128, 5000, 11007])
     c = O.cols(hs, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
-    e["dWg"] = nl2(f64(dwg[:, hs]), c["dWg"])
-    e["dWu"] = nl2(f64(dwu[:, hs]), c["dWu"])
-    e["dWd"] = nl2(f64(dwd[hs, :]), c["dWd"])
-    banner("T=65536: " + " ".join(f"{k}={v:.2e}" for k, v in e.items()))
-    for k, v in e.items():
-        assert v <= 1e-2, (k, v)
+    _check_sampled("T=65536 dWg", got["dWg"], c["dWg"].T)
+    _check_sampled("T=65536 dWu", got["dWu"], c["dWu"].T)
+    _check_sampled("T=65536 dWd", got["dWd"], c["dWd"])
 
 
 def test_planes_over_2GiB_sampled(mlp):
@@ -169,18 +203,16 @@ def test_planes_over_2GiB_sampled(mlp):
     f = _np(inp)
     banner(f"T={T}: oracle rows and hidden units")
     r = O.rows(rows, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
-    e = {"Y": nl2(f64(y[rows]), r["Y"]), "dI": nl2(f64(dx[rows]), r["dI"]), "G": nl2(f64(G_s), r["G"]),
-         "U": nl2(f64(U_s), r["U"]), "dG": nl2(f64(dG_s), r["dG"]), "dU": nl2(f64(dU_s), r["dU"])}
     a_ref = O.round_to(O.epilogue_fwd(f64(G_s), f64(U_s)), "bf16")
     assert int(O.ulp_distance(f64(A_s), a_ref, "bf16").max()) <= 1
+    got = {"Y": y[rows], "dI": dx[rows], "G": G_s, "U": U_s, "dG": dG_s, "dU": dU_s}
+    for k, v in got.items():
+        _check_sampled(f"T={T} {k}", f64(v), r[k])
     hs = np.array([0, 4999, 11007])
     c = O.cols(hs, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
-    e["dWg"] = nl2(f64(dwg[:, hs]), c["dWg"])
-    e["dWu"] = nl2(f64(dwu[:, hs]), c["dWu"])
-    e["dWd"] = nl2(f64(dwd[hs, :]), c["dWd"])
-    banner(f"T={T}: " + " ".join(f"{k}={v:.2e}" for k, v in e.items()))
-    for k, v in e.items():
-        assert v <= 1e-2, (k, v)
+    _check_sampled(f"T={T} dWg", f64(dwg[:, hs]).T, c["dWg"].T)
+    _check_sampled(f"T={T} dWu", f64(dwu[:, hs]).T, c["dWu"].T)
+    _check_sampled(f"T={T} dWd", f64(dwd[hs, :]), c["dWd"])
 
 
 @pytest.mark.parametrize("D,H", [(1024, 2816), (4096, 11008)])
@@ -193,9 +225,8 @@ def test_no_grad_path(mlp, D, H):
         y = mlp.infer(X.cuda(), Wg, Wu, Wd)
         y_train, _ = mlp.fwd(X.cuda(), Wg, Wu, Wd)
         torch.cuda.synchronize()
-        err = nl2(f64(y), O.infer(X.float().numpy(), f["Wg"], f["Wu"], f["Wd"]))
-        banner(f"infer D={D} S={S}: {err:.2e}")
-        assert err <= 1e-2
+        e = assert_local(f64(y), O.infer(X.float().numpy(), f["Wg"], f["Wu"], f["Wd"]), 1e-2, ("infer", D, S))
+        banner(f"infer D={D} S={S}: {fmt_local(e)}")
         if S > 128:
             # same tiles, same order: the no-grad Y equals the training Y bitwise
             assert torch.equal(y, y_train)
@@ -217,9 +248,9 @@ def test_no_grad_split_k_ragged(mlp, T, D, H):
     y = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"])
     torch.cuda.synchronize()
     f = _np(inp)
-    err = nl2(f64(y), O.infer(f["X"], f["Wg"], f["Wu"], f["Wd"]))
-    banner(f"split-K infer T={T} D={D} H={H}: {err:.2e}")
-    assert err <= 1e-2 and torch.isfinite(y).all()
+    e = assert_local(f64(y), O.infer(f["X"], f["Wg"], f["Wu"], f["Wd"]), 1e-2, ("split-K infer", T, D, H))
+    banner(f"split-K infer T={T} D={D} H={H}: {fmt_local(e)}")
+    assert torch.isfinite(y).all()
 
 
 def test_zero_tokens(mlp):
