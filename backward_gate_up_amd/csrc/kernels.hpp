@@ -38,7 +38,7 @@
 #include "gemm_ring.hpp"
 #include "gemm_skinny.hpp"
 #include "gemm_stream.hpp"
-#include "../../include/swiglu_mlp.h"
+#include "swiglu_mlp.h"
 
 namespace swiglu {
 
@@ -62,7 +62,16 @@ struct KArgs {
   int n_full;      // weight-gradient launch: items (plane-major tiles) run whole
   int ksplit;      // weight-gradient launch: pieces per split tile
   int n_split;     // weight-gradient launch: tiles split over K (items n_full ..)
+  unsigned* zero_ctr;  // no-grad gate/up: arrival counters of the down launch to clear (or nullptr)
+  int n_zero;          // ... and how many
 };
+
+// Workgroup 0 of a no-grad gate/up launch clears the arrival counters that
+// the down launch after it on the stream counts on (see stream_gemm).
+__device__ __forceinline__ void clear_counters(const KArgs& g) {
+  if (g.zero_ctr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < g.n_zero; i += blockDim.x) g.zero_ctr[i] = 0u;
+}
 
 // Logistic function sigma(g) = 1 / (1 + exp(-g)) in fp32, from a stored gate
 // value. IEEE form: expf from the device math library and IEEE division
@@ -1115,6 +1124,7 @@ __global__ void __launch_bounds__((64 * SkinnyCfg<KIND, MT>::W)) skinny_gemm(con
   __shared__ __attribute__((aligned(1024))) char lds[BYTES];
   // consecutive units on one XCD (the hardware deals workgroups round-robin
   // over the 8 XCDs)
+  if constexpr (KIND == GATEUP) clear_counters(g);
   const int nb = gridDim.x, nb8 = nb & ~7;
   int b = blockIdx.x;
   if (b < nb8) b = (b & 7) * (nb8 >> 3) + (b >> 3);
@@ -1122,11 +1132,18 @@ __global__ void __launch_bounds__((64 * SkinnyCfg<KIND, MT>::W)) skinny_gemm(con
 }
 
 // ---------------------------------------------------------------------------
-// Split-K weight streaming for the no-grad forward, T <= 128 (gemm_stream.hpp).
-// KIND GATEUP: weights g.b0 = Wg, g.b1 = Wu; partial planes G, U.
-// KIND PLAIN: weights g.b0; one partial plane.
+// Weight streaming for the no-grad forward, T <= 128 (gemm_stream.hpp).
+// KIND GATEUP: weights g.b0 = Wg, g.b1 = Wu; writes A (and G, U when
+// store_gu). KIND PLAIN: weights g.b0; writes C.
 // g.a0: activations [T, K] (K-contiguous); weights [K, N] (N-contiguous).
-// P: fp32 partials [splits][NW][T][N]. Workgroup b = unit * splits + split.
+// Workgroup b = unit * splits + split streams K steps of its split for the
+// unit's 64 columns. splits == 1: the workgroup owns whole outputs and
+// applies the epilogue itself. splits > 1: each workgroup writes an fp32
+// partial (P: [splits][NW][T][N]) and counts its arrival on ctr[unit]; the
+// last of a unit's workgroups to arrive adds the unit's partials in split
+// order (deterministic), applies the epilogue and leaves the counter at
+// zero. The counters must be zero when the launch starts: the gate/up
+// launch of the same call clears those of the down launch (zero_ctr).
 // ---------------------------------------------------------------------------
 template <int KIND, int MT>
 struct StreamCfg {
@@ -1137,8 +1154,38 @@ struct StreamCfg {
   static constexpr int BYTES = W * NS * C * 1024;
 };
 
+// The epilogue of four consecutive outputs (m, n .. n + 3) from their fp32
+// sums: GATEUP rounds g and u, writes A (and G, U when store_gu); PLAIN
+// writes C.
+template <class E, int KIND>
+__device__ __forceinline__ void stream_store(const KArgs& g, int m, int n, const f32x4_t (&sum)[KIND == GATEUP ? 2 : 1]) {
+  using V4 = typename E::vec4;
+  const int64_t off = ((int64_t)m * g.ldc + n) * E::kBytes;
+  if constexpr (KIND == GATEUP) {
+    V4 gv, uv, av;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      typename E::elem gs = E::from_f32(sum[0][e]);
+      typename E::elem us = E::from_f32(sum[1][e]);
+      gv[e] = gs;
+      uv[e] = us;
+      av[e] = swiglu_a<E>(E::to_f32(gs), E::to_f32(us), g.two_round);
+    }
+    *(V4*)(g.c0 + off) = av;
+    if (g.store_gu) {
+      *(V4*)(g.c1 + off) = gv;
+      *(V4*)(g.c2 + off) = uv;
+    }
+  } else {
+    V4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = E::from_f32(sum[0][e]);
+    *(V4*)(g.c0 + off) = v;
+  }
+}
+
 template <class E, int KIND, int MT>
-__global__ void __launch_bounds__(256) stream_partial(const KArgs g, float* P, int splits) {
+__global__ void __launch_bounds__(256) stream_gemm(const KArgs g, float* P, int splits, unsigned* ctr) {
   using namespace stream;
   using skinny::act_frag;
   using skinny::mfma16;
@@ -1153,6 +1200,7 @@ __global__ void __launch_bounds__(256) stream_partial(const KArgs g, float* P, i
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x / splits, split = blockIdx.x - unit * splits;
+  if constexpr (KIND == GATEUP) clear_counters(g);
   const int n0 = unit * NC;
   const Operand& X = g.a0;
   const int K = X.k, N = g.N, T = g.M;
@@ -1242,10 +1290,12 @@ __global__ void __launch_bounds__(256) stream_partial(const KArgs g, float* P, i
   }
   ring::wait_vmcnt<0>();  // the surplus steps' loads (zeros) have landed too
 
-  // add the waves' sums through LDS, one 16-column block at a time, and
-  // write this workgroup's partial
+  // add the waves' sums through LDS, one 16-column block at a time; then
+  // either apply the epilogue (whole K here) or write this workgroup's
+  // partial
   constexpr int NB = NW * MT;  // 1-KiB blocks of f32x4 per wave and column block
   char* part = lds + wave * (NB * 1024);
+  const bool direct = splits == 1;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     ring::lds_barrier();  // the ring (or the previous block's sums) is no longer read
@@ -1254,58 +1304,70 @@ __global__ void __launch_bounds__(256) stream_partial(const KArgs g, float* P, i
 #pragma unroll
       for (int t = 0; t < MT; ++t) *(f32x4_t*)(part + ((w * MT + t) * 64 + lane) * 16) = acc[w][c][t];
     ring::lds_barrier();
-    for (int blk = wave; blk < NB; blk += W) {
-      f32x4_t sum = f32x4_t{};
+    // 16x16 output block of token tile t: token t * 16 + lane % 16, columns
+    // 16 c + 4 (lane / 16) .. + 3
+    const int n = n0 + c * 16 + (lane >> 4) * 4;
+    if (direct) {
+      for (int t = wave; t < MT; t += W) {
+        f32x4_t sum[NW];
 #pragma unroll
-      for (int v = 0; v < W; ++v) sum += *(const f32x4_t*)(lds + v * (NB * 1024) + (blk * 64 + lane) * 16);
-      const int w = blk / MT, t = blk % MT;
-      // 16x16 output block: token t * 16 + lane % 16, columns 16 c + 4 (lane / 16) .. + 3
-      const int m = t * 16 + (lane & 15);
-      const int n = n0 + c * 16 + (lane >> 4) * 4;
-      if (m < T && n < N) *(f32x4_t*)(P + (((int64_t)split * NW + w) * T + m) * N + n) = sum;
+        for (int w = 0; w < NW; ++w) {
+          sum[w] = f32x4_t{};
+#pragma unroll
+          for (int v = 0; v < W; ++v) sum[w] += *(const f32x4_t*)(lds + v * (NB * 1024) + ((w * MT + t) * 64 + lane) * 16);
+        }
+        const int m = t * 16 + (lane & 15);
+        if (m < T && n < N) stream_store<E, KIND>(g, m, n, sum);
+      }
+    } else {
+      for (int blk = wave; blk < NB; blk += W) {
+        f32x4_t sum = f32x4_t{};
+#pragma unroll
+        for (int v = 0; v < W; ++v) sum += *(const f32x4_t*)(lds + v * (NB * 1024) + (blk * 64 + lane) * 16);
+        const int w = blk / MT, t = blk % MT;
+        const int m = t * 16 + (lane & 15);
+        if (m < T && n < N) {
+          // device-coherent stores (they bypass this XCD's L2), read back by
+          // another workgroup of the unit
+          float* q = P + (((int64_t)split * NW + w) * T + m) * N + n;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) __hip_atomic_store(q + e, sum[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
   }
-}
+  if (direct) return;
 
-// Sum the partials of each output in split order and apply the epilogue:
-// GATEUP writes A (and G, U when store_gu), PLAIN writes C. One thread per 4
-// consecutive outputs of a row.
-template <class E, int KIND>
-__global__ void __launch_bounds__(256) stream_reduce(const KArgs g, const float* P, int splits) {
-  constexpr int NW = KIND == GATEUP ? 2 : 1;
-  const int T = g.M, N = g.N;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nq = (int64_t)T * (N / 4);
-  if (i >= nq) return;
-  const int m = (int)(i / (N / 4)), n = (int)(i % (N / 4)) * 4;
-  f32x4_t sum[NW];
+  // Arrival. The partials went out as device-coherent stores; each wave
+  // waits until its own have completed, the barrier then orders all of them
+  // before thread 0's atomic add on the unit's counter. The workgroup that
+  // brings the count to `splits` is the last: it reads the partials with
+  // device-coherent loads, so no cache of its CU or XCD can serve stale
+  // data, and no cache write-back or invalidation is needed anywhere.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // (also: every wave is done reading the LDS sums)
+  int* last_arrival = (int*)lds;
+  if (threadIdx.x == 0)
+    *last_arrival = __hip_atomic_fetch_add(ctr + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (unsigned)(splits - 1);
+  __syncthreads();
+  if (!*last_arrival) return;
+  if (threadIdx.x == 0) __hip_atomic_store(ctr + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the unit's T x 64 outputs, four consecutive columns per thread
+  for (int i = threadIdx.x; i < T * (NC / 4); i += 256) {
+    const int m = i / (NC / 4), n = n0 + (i % (NC / 4)) * 4;
+    if (n >= N) continue;
+    f32x4_t sum[NW];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    sum[w] = f32x4_t{};
-    for (int s = 0; s < splits; ++s) sum[w] += *(const f32x4_t*)(P + (((int64_t)s * NW + w) * T + m) * N + n);
-  }
-  using V4 = typename E::vec4;
-  const int64_t off = ((int64_t)m * g.ldc + n) * E::kBytes;
-  if constexpr (KIND == GATEUP) {
-    V4 gv, uv, av;
+    for (int w = 0; w < NW; ++w) {
+      sum[w] = f32x4_t{};
+      for (int sp = 0; sp < splits; ++sp) {
+        float* q = P + (((int64_t)sp * NW + w) * T + m) * N + n;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      typename E::elem gs = E::from_f32(sum[0][e]);
-      typename E::elem us = E::from_f32(sum[1][e]);
-      gv[e] = gs;
-      uv[e] = us;
-      av[e] = swiglu_a<E>(E::to_f32(gs), E::to_f32(us), g.two_round);
+        for (int e = 0; e < 4; ++e) sum[w][e] += __hip_atomic_load(q + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    *(V4*)(g.c0 + off) = av;
-    if (g.store_gu) {
-      *(V4*)(g.c1 + off) = gv;
-      *(V4*)(g.c2 + off) = uv;
-    }
-  } else {
-    V4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = E::from_f32(sum[0][e]);
-    *(V4*)(g.c0 + off) = v;
+    stream_store<E, KIND>(g, m, n, sum);
   }
 }
 
@@ -1510,42 +1572,76 @@ static int launch_skinny(KArgs a, int64_t T, int64_t ncols, hipStream_t stream) 
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
-// Split-K streaming launch (no-grad, 16-bit, T <= 128): partials into P, then
-// the reduction with the epilogue; timed as one stage.
+// Streaming launch (no-grad, 16-bit, T <= 128): `splits` workgroups per
+// 64-column unit; see stream_gemm. One launch per stage.
+struct StreamArgs {
+  int splits;     // K splits per unit (1: no partials)
+  float* P;       // fp32 partials (splits > 1)
+  unsigned* ctr;  // arrival counters, one per unit (splits > 1), zero at launch
+};
+
 template <class E, int KIND, int MT>
-static void launch_stream_mt(const KArgs& a, int grid, int splits, float* P, hipStream_t stream) {
-  hipLaunchKernelGGL((stream_partial<E, KIND, MT>), dim3(grid), dim3(256), 0, stream, a, P, splits);
+static void launch_stream_mt(const KArgs& a, int grid, const StreamArgs& st, hipStream_t stream) {
+  hipLaunchKernelGGL((stream_gemm<E, KIND, MT>), dim3(grid), dim3(256), 0, stream, a, st.P, st.splits, st.ctr);
 }
 template <class E, int KIND, int STAGE>
-static int launch_stream(KArgs a, int64_t T, int64_t ncols, float* P, hipStream_t stream) {
+static int launch_stream(KArgs a, int64_t T, int64_t ncols, const StreamArgs& st, hipStream_t stream) {
   const int units = cdiv(ncols, stream::NC);
-  const int splits = stream::splits_for(units, cdiv(a.a0.k, stream::KS), StreamCfg<KIND, 1>::W);
   if (units <= 0 || T <= 0) return SWIGLU_OK;
   StageScope scope(STAGE, stream);
-  if (T <= 16) launch_stream_mt<E, KIND, 1>(a, units * splits, splits, P, stream);
-  else if (T <= 32) launch_stream_mt<E, KIND, 2>(a, units * splits, splits, P, stream);
-  else if (T <= 64) launch_stream_mt<E, KIND, 4>(a, units * splits, splits, P, stream);
-  else launch_stream_mt<E, KIND, 8>(a, units * splits, splits, P, stream);
-  if (hipGetLastError() != hipSuccess) return SWIGLU_ERR_LAUNCH;
-  const int64_t nq = T * (ncols / 4);
-  hipLaunchKernelGGL((stream_reduce<E, KIND>), dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream, a, P, splits);
+  const int grid = units * st.splits;
+  if (T <= 16) launch_stream_mt<E, KIND, 1>(a, grid, st, stream);
+  else if (T <= 32) launch_stream_mt<E, KIND, 2>(a, grid, st, stream);
+  else if (T <= 64) launch_stream_mt<E, KIND, 4>(a, grid, st, stream);
+  else launch_stream_mt<E, KIND, 8>(a, grid, st, stream);
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
 // Tokens up to which the forward runs on the weight-streaming kernels
-// (training: few_t; no-grad, which has a workspace for partial sums: stream_t).
+// (training: few_t; no-grad, which has a workspace: stream_t).
 static inline bool few_t(int64_t T) { return T <= 64; }
 static inline bool stream_t(int64_t T) { return T <= 128; }
-
-// fp32 partials of the split-K no-grad path (16-bit, T <= 128): the larger of
-// the gate/up (2 planes of [T, H]) and down ([T, D]) stages, placed after the
-// A plane in the no-grad workspace (256-byte aligned).
 static inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-static inline size_t stream_partial_bytes(int64_t T, int64_t D, int64_t H) {
-  const int sg = stream::splits_for(cdiv(H, stream::NC), cdiv(D, stream::KS), 4);
-  const int sd = stream::splits_for(cdiv(D, stream::NC), cdiv(H, stream::KS), 4);
-  const size_t pg = (size_t)sg * 2 * T * H * 4, pd = (size_t)sd * T * D * 4;
-  return pg > pd ? pg : pd;
+
+// No-grad gate/up with few tokens and a narrow hidden dimension: the
+// few-token kernel (16-column units, up to 16 waves splitting K) gives more,
+// shorter weight streams than 64-column units would.
+constexpr int kInferSkinnyMaxH = 4096;
+static inline bool infer_gateup_skinny(int64_t T, int64_t H) { return few_t(T) && H <= kInferSkinnyMaxH; }
+
+// Largest fp32 partial buffer of the no-grad down projection, as a multiple
+// of the call's A + Y bytes: the split count is capped so that the
+// intermediate memory of a call (workspace + Y) stays within 3 (A + Y).
+// Measured at D = 4096, H = 11008 (3 splits): the down projection takes
+// 24-59 us for S = 1-128 against 45-110 us unsplit; more splits were no
+// faster at S = 1 and slower from S = 64 on (the last arrival's reduction
+// grows with them).
+constexpr int kInferPartialCap = 2;
+
+// No-grad workspace. The A plane [T, H]; for 16-bit with T <= 128 (weight
+// streaming) also the down projection's arrival counters and, when its K is
+// split, its fp32 partials, each 256-byte aligned after A. The gate/up stage
+// never splits K: the hidden dimension alone gives enough 64-column units.
+struct InferPlan {
+  size_t a_bytes = 0, ctr_off = 0, p_off = 0, total = 0;
+  int down_units = 0, down_splits = 1;
+};
+static inline InferPlan infer_plan(int64_t T, int64_t D, int64_t H, size_t e) {
+  InferPlan p;
+  p.a_bytes = (size_t)T * H * e;
+  p.total = p.a_bytes;
+  if (e != 2 || T <= 0 || !stream_t(T)) return p;
+  p.down_units = cdiv(D, stream::NC);
+  int sp = stream::splits_for(p.down_units, cdiv(H, stream::KS), StreamCfg<PLAIN, 1>::W);
+  const size_t per = (size_t)T * D * 4;                                    // one split's partials
+  const size_t cap = (size_t)kInferPartialCap * (size_t)T * (H + D) * e;  // x (A + Y)
+  const int sp_mem = (int)(cap / per);
+  if (sp > sp_mem) sp = sp_mem < 1 ? 1 : sp_mem;
+  p.down_splits = sp;
+  p.ctr_off = align256(p.a_bytes);
+  p.p_off = align256(p.ctr_off + (size_t)p.down_units * 4);
+  p.total = sp > 1 ? p.p_off + (size_t)sp * per : p.ctr_off + (size_t)p.down_units * 4;
+  return p;
 }
 
 // Rows of X per workgroup tile for the T-indexed GEMMs. Small token counts
@@ -1559,8 +1655,8 @@ struct Path {
 
   template <int STAGE>
   static int gateup(const void* X, const void* Wg, const void* Wu, char* Ap, char* Gp, char* Up,
-                    int64_t T, int64_t D, int64_t H, bool store_gu, bool two_round, float* P,
-                    hipStream_t s) {
+                    int64_t T, int64_t D, int64_t H, bool store_gu, bool two_round, const StreamArgs* st,
+                    hipStream_t s, unsigned* zero_ctr = nullptr, int n_zero = 0) {
     KArgs a{};
     a.a0 = opnd(X, D, T, D);
     a.b0 = opnd(Wg, H, H, D);
@@ -1573,8 +1669,15 @@ struct Path {
     a.N = (int)H;
     a.store_gu = store_gu ? 1 : 0;
     a.two_round = two_round ? 1 : 0;
+    a.zero_ctr = zero_ctr;
+    a.n_zero = n_zero;
     if constexpr (E::kBytes == 2) {
-      if (P && stream_t(T)) return launch_stream<E, GATEUP, STAGE>(a, T, H, P, s);
+      // (the streaming kernels are instantiated for the no-grad stage only)
+      if constexpr (STAGE == 6)
+        if (st) {
+          if (infer_gateup_skinny(T, H)) return launch_skinny<E, GATEUP, STAGE>(a, T, H, s);
+          return launch_stream<E, GATEUP, STAGE>(a, T, H, *st, s);
+        }
       if (few_t(T)) return launch_skinny<E, GATEUP, STAGE>(a, T, H, s);
     }
     if (small_t(T)) {
@@ -1589,8 +1692,8 @@ struct Path {
   }
 
   template <int STAGE>
-  static int down(const char* Ap, const void* Wd, void* Y, int64_t T, int64_t D, int64_t H, float* P,
-                  hipStream_t s) {
+  static int down(const char* Ap, const void* Wd, void* Y, int64_t T, int64_t D, int64_t H,
+                  const StreamArgs* st, hipStream_t s) {
     KArgs a{};
     a.a0 = opnd(Ap, H, T, H);
     a.b0 = opnd(Wd, D, D, H);
@@ -1599,7 +1702,8 @@ struct Path {
     a.M = (int)T;
     a.N = (int)D;
     if constexpr (E::kBytes == 2) {
-      if (P && stream_t(T)) return launch_stream<E, PLAIN, STAGE>(a, T, D, P, s);
+      if constexpr (STAGE == 7)
+        if (st) return launch_stream<E, PLAIN, STAGE>(a, T, D, *st, s);
       if (few_t(T)) return launch_skinny<E, PLAIN, STAGE>(a, T, D, s);
     }
     if (small_t(T)) {
@@ -1760,12 +1864,21 @@ int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const
 
 template <class E>
 int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws, int64_t T,
-                     int64_t D, int64_t H, bool two_round, hipStream_t s) {
+              int64_t D, int64_t H, bool two_round, hipStream_t s) {
   char* Ap = (char*)ws;
-  float* P = (E::kBytes == 2 && stream_t(T)) ? (float*)(Ap + align256((size_t)T * H * E::kBytes)) : nullptr;
-  int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, P, s);
+  const InferPlan pl = infer_plan(T, D, H, E::kBytes);
+  if (pl.down_units == 0) {
+    int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, nullptr, s);
+    if (rc) return rc;
+    return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, nullptr, s);
+  }
+  unsigned* ctr = (unsigned*)(Ap + pl.ctr_off);
+  const StreamArgs sg{1, nullptr, nullptr};
+  const StreamArgs sd{pl.down_splits, pl.down_splits > 1 ? (float*)(Ap + pl.p_off) : nullptr, ctr};
+  int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, &sg, s, ctr,
+                                       pl.down_units);
   if (rc) return rc;
-  return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, P, s);
+  return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, &sd, s);
 }
 
 }  // namespace swiglu

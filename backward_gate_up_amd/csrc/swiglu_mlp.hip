@@ -109,9 +109,7 @@ size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype) {
 size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype) {
   size_t e = elt_bytes(dtype);
   if (!e || T < 0 || D <= 0 || H <= 0) return 0;
-  const size_t a = (size_t)T * (size_t)H * e;
-  if (e == 2 && T > 0 && stream_t(T)) return align256(a) + stream_partial_bytes(T, D, H);
-  return a;
+  return infer_plan(T, D, H, e).total;
 }
 
 size_t swiglu_mlp_bwd_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype) {

@@ -121,19 +121,39 @@ def cpu_baseline(inp, D, H, target_s):
                       f"{t:.1f} s, numpy float64 BLAS"}
 
 
-def infer_sweep(mlp, torch, dev, reps=20):
+def stream_copy_gbps(torch, dev, mib=1024, reps=10):
+    """A plain device-to-device copy of `mib` MiB (read + write), timed with
+    HIP events in the same run: the achievable-bandwidth reference for the
+    no-grad rows (GB/s counts both directions)."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(2 * (mib << 20) / (ms * 1e-3) / 1e9, 1)
+
+
+def infer_sweep(mlp, torch, dev, reps=20, copy_gbps=None):
     """No-grad path at B=1, S in {1..256}, D/H in {1024/2816, 4096/11008}: device
     time per call (HIP events around the call only) with the 256 MB Infinity
     Cache flushed before every timed call by reading a 1 GiB buffer outside the
     events, and HBM GB/s from the call's algorithmic bytes
-    2*(3*D*H + 2*T*D + 2*T*H). A flush that writes leaves the caches full of
-    dirty lines whose write-back then competes with the call's reads; that
-    time is reported beside it (us_write_flush).
+    2*(3*D*H + 2*T*D + 2*T*H), against 8 TB/s and against the same run's
+    stream copy. A flush that writes leaves the caches full of dirty lines
+    whose write-back then competes with the call's reads; that time is
+    reported beside it (us_write_flush).
     Also the host-inclusive wall time of one call (Python binding, argument
-    checks, two launches, completion), eagerly and as a replay of a HIP graph
+    checks, the launches, completion), eagerly and as a replay of a HIP graph
     that captured the same call (checked bitwise against the eager output),
-    and the intermediate bytes the call needs (workspace + Y; the workspace is
-    A, plus fp32 partial sums of the split-K kernels for S <= 128)."""
+    measured alternately after warm-up replays, and the intermediate memory
+    of the call (workspace + Y) beside A + Y."""
     from synth import INFER_DH, INFER_S, make_inputs
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -148,6 +168,7 @@ def infer_sweep(mlp, torch, dev, reps=20):
             ws = torch.empty(mlp.infer_workspace_bytes(S, D, H), dtype=torch.uint8, device=dev)
             for _ in range(3):
                 mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+
             def device_us(write):
                 ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                       for _ in range(reps)]
@@ -167,18 +188,6 @@ def infer_sweep(mlp, torch, dev, reps=20):
             med_w = device_us(True)
             nbytes = 2 * (3 * D * H + 2 * S * D + 2 * S * H)
 
-            def wall(call):
-                ts = []
-                for _ in range(reps):
-                    flush.sum()
-                    torch.cuda.synchronize()
-                    t0 = time.perf_counter()
-                    call()
-                    torch.cuda.synchronize()
-                    ts.append((time.perf_counter() - t0) * 1e6)
-                return sorted(ts)[len(ts) // 2]
-
-            eager_us = wall(lambda: mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws))
             y_eager = y.clone()
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
@@ -187,14 +196,31 @@ def infer_sweep(mlp, torch, dev, reps=20):
             graph.replay()
             torch.cuda.synchronize()
             same = bool(torch.equal(y, y_eager))
-            graph_us = wall(graph.replay)
+            for _ in range(5):
+                graph.replay()
+            torch.cuda.synchronize()
+            eager_call = lambda: mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+            t_e, t_g = [], []
+            for _ in range(reps):
+                for call, ts in ((eager_call, t_e), (graph.replay, t_g)):
+                    flush.sum()
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    call()
+                    torch.cuda.synchronize()
+                    ts.append((time.perf_counter() - t0) * 1e6)
             del graph
+            gbps = nbytes / (med * 1e-6) / 1e9
+            a_y = 2 * S * (H + D)
+            inter = ws.numel() + 2 * S * D
             rows[str(S)] = {"us": round(med, 2), "us_write_flush": round(med_w, 2),
-                            "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                            "frac_hbm": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
-                            "wall_us_eager": round(eager_us, 1), "wall_us_graph": round(graph_us, 1),
+                            "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBS, 3),
+                            "frac_copy": round(gbps / copy_gbps, 3) if copy_gbps else None,
+                            "wall_us_eager": round(sorted(t_e)[reps // 2], 1),
+                            "wall_us_graph": round(sorted(t_g)[reps // 2], 1),
                             "graph_bitwise_equal": same,
-                            "intermediate_MiB": round((ws.numel() + 2 * S * D) / 2**20, 3)}
+                            "intermediate_MiB": round(inter / 2**20, 3),
+                            "intermediate_over_A_plus_Y": round(inter / a_y, 3)}
         out[f"{D}x{H}"] = rows
     del flush
     return out
@@ -335,6 +361,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-infer", action="store_true", help="skip the no-grad (inference) sweep")
+    ap.add_argument("--infer-only", action="store_true",
+                    help="only the no-grad sweep (and the stream-copy reference): one JSON line")
     ap.add_argument("--no-fp32", action="store_true", help="skip the true-IEEE fp32 run")
     ap.add_argument("--no-tp", action="store_true", help="skip the tensor-parallel shard-shape sweep")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -351,6 +379,14 @@ def main():
 
     import backward_gate_up_amd as mlp
     from synth import WORKLOADS, workload_inputs
+
+    if args.infer_only:
+        dev = torch.device("cuda:0")
+        copy = stream_copy_gbps(torch, dev)
+        print(json.dumps({"metric": "no-grad HBM GB/s (B=1, 256 MB cache flushed per call by a 1 GiB read)",
+                          "unit": "GB/s", "peak_GBps": PEAK_HBM_GBS, "stream_copy_GBps": copy,
+                          "by_shape": infer_sweep(mlp, torch, dev, copy_gbps=copy)}), flush=True)
+        return
 
     name = "mlp_4096x11008_T65536"
     D, H, B, S, _ = WORKLOADS[name]
@@ -444,8 +480,10 @@ def main():
     if not args.no_tp:
         out["tp_shards"] = tp_shard_sweep(mlp, torch, dev, T, D, H)
     if not args.no_infer:
+        copy = stream_copy_gbps(torch, dev)
         out["infer"] = {"metric": "no-grad HBM GB/s (B=1, 256 MB cache flushed per call by a 1 GiB read)",
-                        "peak_GBps": PEAK_HBM_GBS, "by_shape": infer_sweep(mlp, torch, dev)}
+                        "peak_GBps": PEAK_HBM_GBS, "stream_copy_GBps": copy,
+                        "by_shape": infer_sweep(mlp, torch, dev, copy_gbps=copy)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, D, H, args.cpu_seconds)
     print(json.dumps(out), flush=True)

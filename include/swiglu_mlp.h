@@ -95,9 +95,11 @@ size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
 /* Bytes of the no-grad workspace: the A plane, T * H * sizeof(dtype) ("a
  * dedicated no-grad path that does not save G/U", issue #1347, "Summary";
  * the page's table "Inference, BF16, B=1" equals A + Y at S = 256). For
- * bf16/fp16 with 1 <= T <= 128 it also holds the fp32 partial sums of the
- * split-K weight-streaming kernels (after A, 256-byte aligned): at most
- * about 34 MB at D = 4096, H = 11008, T = 128. 0 on bad args. */
+ * bf16/fp16 with 1 <= T <= 128 (weight streaming) it also holds, after A and
+ * 256-byte aligned, one arrival counter per 64 columns of the down
+ * projection and the fp32 partial sums of its K splits, capped so that
+ * workspace + Y stays within 3 (A + Y) (D = 4096, H = 11008, T = 128:
+ * 10.2 MB against A + Y = 3.9 MB). 0 on bad args. */
 size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
 
 /* Bytes of the backward workspace: fp32 partial tiles (256 x 256, 256 KiB
@@ -137,8 +139,10 @@ int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
 
 /* No-grad forward: Y [T, D] from X and the weights; G and U are never
  * stored. workspace (>= swiglu_mlp_infer_workspace_bytes bytes) holds A and,
- * for T <= 128, partial sums; its contents on entry do not matter. Y must not
- * overlap the inputs or the workspace. */
+ * for T <= 128, counters and partial sums; its contents on entry do not
+ * matter (the call clears what it counts on). Two launches. Calls that use
+ * one workspace must not overlap (stream order them). Y must not overlap
+ * the inputs or the workspace. */
 int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd,
                      void* Y, void* workspace, size_t workspace_bytes,
                      int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream);

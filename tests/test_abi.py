@@ -167,3 +167,21 @@ def test_shape_limits_of_32_bit_lane_offsets():
     # the tile count of a launch must fit in int32
     assert L.swiglu_mlp_fwd(*far[:3], far[3] + 8, *far[4:], (1 << 31) - 1, 8, 8, 0, None) == 4
     assert L.swiglu_mlp_fwd(*far, (1 << 31) - 1, 4194296, 64, 0, None) == 2
+
+
+def test_no_grad_intermediate_memory_bound():
+    """No-grad intermediate memory (workspace + Y) at B=1, S = 1 ... 256 for
+    both inference shapes of the pages: within 3 (A + Y) at every S (the
+    split-K partials of the down projection are capped), and exactly A + Y
+    where no K is split (S = 256, and fp32). The pages' table ("[RFC]
+    Full-pipeline SwiGLU MLP ...", "Intermediate-memory results") gives A + Y
+    at S = 256."""
+    L = _lib()
+    for D, H in ((1024, 2816), (4096, 11008)):
+        for S in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+            a_y = 2 * S * (H + D)
+            ws = L.swiglu_mlp_infer_workspace_bytes(S, D, H, 0)
+            assert ws >= 2 * S * H
+            assert ws + 2 * S * D <= 3 * a_y, (D, S, ws)
+            assert L.swiglu_mlp_infer_workspace_bytes(S, D, H, 2) == 4 * S * H
+        assert L.swiglu_mlp_infer_workspace_bytes(256, D, H, 0) + 2 * 256 * D == 2 * 256 * (H + D)
