@@ -20,7 +20,7 @@ import torch
 from . import _lib as _L
 from ._lib import SwiGLUError, STAGE_NAMES, NUM_STAGES  # noqa: F401
 
-__all__ = ["fwd", "bwd", "infer", "SwiGLUMLPFunction", "swiglu_mlp", "SwiGLUMLP", "saved_bytes",
+__all__ = ["fwd", "bwd", "infer", "infer_noalloc", "SwiGLUMLPFunction", "swiglu_mlp", "SwiGLUMLP", "saved_bytes",
            "infer_workspace_bytes", "bwd_workspace_bytes", "SwiGLUError", "StageTimer"]
 
 _DT = {torch.bfloat16: _L.BF16, torch.float16: _L.FP16, torch.float32: _L.FP32}
@@ -145,6 +145,20 @@ def infer(x, wg, wu, wd, y=None, workspace=None, two_round=False):
     rc = _L.lib().swiglu_mlp_infer_ex(_p(x), _p(wg), _p(wu), _p(wd), _p(y), _p(workspace), nbytes,
                                       T, D, H, _dt(x), _flags(two_round), _stream(x.device))
     _check(rc, "swiglu_mlp_infer_ex")
+    return y
+
+
+def infer_noalloc(x, wg, wu, wd, y=None, two_round=False):
+    """No-grad forward through the allocation-free entry point: the library's
+    fixed per-device scratch holds the workspace (calls on one device must
+    not overlap). Raises SwiGLUError (SWIGLU_ERR_SCRATCH) when the shape
+    needs more than that scratch."""
+    x, wg, wu, wd = (t.contiguous() for t in (x, wg, wu, wd))
+    T, D, H = _shapes(x, wg, wu, wd)
+    y = _buf(y, (T, D), x, "y")
+    rc = _L.lib().swiglu_mlp_infer_noalloc(_p(x), _p(wg), _p(wu), _p(wd), _p(y), T, D, H, _dt(x),
+                                           _flags(two_round), _stream(x.device))
+    _check(rc, "swiglu_mlp_infer_noalloc")
     return y
 
 

@@ -10,8 +10,9 @@ BF16, FP16, FP32 = 0, 1, 2
 STATUS = {
     0: "SWIGLU_OK", 1: "SWIGLU_ERR_NULL", 2: "SWIGLU_ERR_SHAPE", 3: "SWIGLU_ERR_DTYPE",
     4: "SWIGLU_ERR_ALIGN", 5: "SWIGLU_ERR_ALIAS", 6: "SWIGLU_ERR_WORKSPACE",
-    7: "SWIGLU_ERR_DEVICE", 8: "SWIGLU_ERR_LAUNCH", 9: "SWIGLU_ERR_FLAGS",
+    7: "SWIGLU_ERR_DEVICE", 8: "SWIGLU_ERR_LAUNCH", 9: "SWIGLU_ERR_FLAGS", 10: "SWIGLU_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20
 FLAG_TWO_ROUND = 1
 NUM_STAGES = 10
 STAGE_NAMES = ("gateup_swiglu", "down_proj", "dgu_inplace", "dwd", "dwgu", "dx",
@@ -55,6 +56,8 @@ def lib():
     L.swiglu_mlp_fwd_ex.restype = i32
     L.swiglu_mlp_infer_ex.argtypes = [vp] * 6 + [sz] + [i64] * 3 + [i32, u32, vp]
     L.swiglu_mlp_infer_ex.restype = i32
+    L.swiglu_mlp_infer_noalloc.argtypes = [vp] * 5 + [i64] * 3 + [i32, u32, vp]
+    L.swiglu_mlp_infer_noalloc.restype = i32
     L.swiglu_mlp_status_string.argtypes = [i32]
     L.swiglu_mlp_status_string.restype = ctypes.c_char_p
     L.swiglu_mlp_timer_start.argtypes = [i32]

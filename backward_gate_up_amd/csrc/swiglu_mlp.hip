@@ -1,6 +1,8 @@
 // swiglu_mlp.hip -- the C ABI of include/swiglu_mlp.h: argument validation,
 // size queries, dispatch to the per-dtype drivers (defined in
 // instantiate.hip builds) and the stage timer.
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace swiglu {
@@ -92,6 +94,30 @@ static int zero_fill(void* p, size_t bytes, hipStream_t s) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_zero, dim3(blocks), dim3(256), 0, s, (u32x4_t*)p, n16);
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+// ---- fixed scratch of the allocation-free no-grad entry point -------------
+// The no-grad workspace of swiglu_mlp_infer_noalloc lives in this array,
+// one copy per device, held until the process ends. In host code its name
+// is only a host-side stand-in: the device address of this device's copy
+// comes from hipGetSymbolAddress (once per device, with that device
+// current), and only that address is ever handed to kernels.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[SWIGLU_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SWIGLU_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SWIGLU_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SWIGLU_OK;
 }
 
 }  // namespace swiglu
@@ -218,6 +244,32 @@ int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* 
   return swiglu_mlp_infer_ex(X, Wg, Wu, Wd, Y, workspace, workspace_bytes, T, D, H, dtype, 0u, stream);
 }
 
+int swiglu_mlp_infer_noalloc(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, int64_t T,
+                             int64_t D, int64_t H, int dtype, unsigned flags, hipStream_t stream) {
+  size_t e = elt_bytes(dtype);
+  if (!e) return SWIGLU_ERR_DTYPE;
+  if (flags & ~SWIGLU_FLAGS_ALL) return SWIGLU_ERR_FLAGS;
+  int rc = check_shape(T, D, H, e);
+  if (rc) return rc;
+  const size_t need = swiglu_mlp_infer_workspace_bytes(T, D, H, dtype);
+  if (need > SWIGLU_NOALLOC_SCRATCH_BYTES) return SWIGLU_ERR_SCRATCH;
+  Range in[] = {{X, (size_t)T * D * e}, {Wg, (size_t)D * H * e}, {Wu, (size_t)D * H * e}, {Wd, (size_t)H * D * e}};
+  Range yr[] = {{Y, (size_t)T * D * e}};
+  if ((rc = check_ptrs(in, 4)) || (rc = check_ptrs(yr, 1))) return rc;
+  for (auto& i : in)
+    if (overlap(yr[0], i)) return SWIGLU_ERR_ALIAS;
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  // the scratch is not the caller's memory, but the inputs and Y must not
+  // lie in it either
+  Range sr{ws, need};
+  if (overlap(yr[0], sr)) return SWIGLU_ERR_ALIAS;
+  for (auto& i : in)
+    if (overlap(i, sr)) return SWIGLU_ERR_ALIAS;
+  return swiglu_mlp_infer_ex(X, Wg, Wu, Wd, Y, ws, SWIGLU_NOALLOC_SCRATCH_BYTES, T, D, H, dtype, flags, stream);
+}
+
 const char* swiglu_mlp_status_string(int status) {
   switch (status) {
     case SWIGLU_OK: return "ok";
@@ -231,6 +283,9 @@ const char* swiglu_mlp_status_string(int status) {
     case SWIGLU_ERR_DEVICE: return "current device is not gfx950 (or a HIP device query failed)";
     case SWIGLU_ERR_LAUNCH: return "kernel launch failed";
     case SWIGLU_ERR_FLAGS: return "unknown bits in flags";
+    case SWIGLU_ERR_SCRATCH:
+      return "the call needs more than the fixed scratch of the allocation-free entry point (see "
+             "SWIGLU_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

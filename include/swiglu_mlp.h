@@ -74,7 +74,8 @@ typedef enum {
   SWIGLU_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required */
   SWIGLU_ERR_DEVICE = 7,    /* current device is not gfx950, or a HIP query failed */
   SWIGLU_ERR_LAUNCH = 8,    /* a kernel launch failed (work may be partially enqueued) */
-  SWIGLU_ERR_FLAGS = 9      /* unknown bits in the flags of an _ex entry point */
+  SWIGLU_ERR_FLAGS = 9,     /* unknown bits in the flags of an _ex entry point */
+  SWIGLU_ERR_SCRATCH = 10   /* swiglu_mlp_infer_noalloc: the call needs more than its fixed scratch */
 } swiglu_status_t;
 
 /* Flags of swiglu_mlp_fwd_ex / swiglu_mlp_infer_ex.
@@ -153,6 +154,25 @@ int swiglu_mlp_infer_ex(const void* X, const void* Wg, const void* Wu, const voi
                         void* Y, void* workspace, size_t workspace_bytes,
                         int64_t T, int64_t D, int64_t H, int dtype, unsigned flags,
                         hipStream_t stream);
+
+/* Allocation-free no-grad forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same computation, kernels and results as
+ * swiglu_mlp_infer_ex with the same flags, but the workspace is a fixed
+ * array of SWIGLU_NOALLOC_SCRATCH_BYTES inside the library: one copy per
+ * device, held from the library's first call on that device until the
+ * process ends. Calls allocate nothing (no hipMalloc, hipFree or allocating
+ * library routine). A call whose swiglu_mlp_infer_workspace_bytes exceeds
+ * the scratch returns SWIGLU_ERR_SCRATCH with nothing launched (bf16 at
+ * D = 4096, H = 11008: every T <= 128, and T <= 1524 above that). The
+ * caller passes the inputs and Y as for swiglu_mlp_infer. Every call on one
+ * device shares that device's scratch, which keeps the last call's
+ * contents (the call clears what it counts on): calls that overlap on one
+ * device race and must be ordered (one stream, or events). */
+#define SWIGLU_NOALLOC_SCRATCH_BYTES (32u << 20)
+int swiglu_mlp_infer_noalloc(const void* X, const void* Wg, const void* Wu, const void* Wd,
+                             void* Y, int64_t T, int64_t D, int64_t H, int dtype,
+                             unsigned flags, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* swiglu_mlp_status_string(int status);

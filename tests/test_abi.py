@@ -69,7 +69,7 @@ def test_infer_memory_matches_pages_table():
 
 def test_status_strings():
     L = _lib()
-    for s in range(10):
+    for s in range(11):
         assert len(L.swiglu_mlp_status_string(s)) > 0
     assert L.swiglu_mlp_status_string(99) == b"unknown status"
 
@@ -185,3 +185,20 @@ def test_no_grad_intermediate_memory_bound():
             assert ws + 2 * S * D <= 3 * a_y, (D, S, ws)
             assert L.swiglu_mlp_infer_workspace_bytes(S, D, H, 2) == 4 * S * H
         assert L.swiglu_mlp_infer_workspace_bytes(256, D, H, 0) + 2 * 256 * D == 2 * 256 * (H + D)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """The allocation-free no-grad entry point checks its fixed scratch on
+    the host: a shape whose workspace exceeds it returns SWIGLU_ERR_SCRATCH
+    before anything else that touches a device."""
+    from backward_gate_up_amd._lib import NOALLOC_SCRATCH_BYTES
+
+    L = _lib()
+    b = [BASE + (i << 36) for i in range(5)]
+    D, H = 4096, 11008
+    assert L.swiglu_mlp_infer_workspace_bytes(1524, D, H, 0) <= NOALLOC_SCRATCH_BYTES
+    assert L.swiglu_mlp_infer_workspace_bytes(1525, D, H, 0) > NOALLOC_SCRATCH_BYTES
+    assert L.swiglu_mlp_infer_noalloc(*b, 1525, D, H, 0, 0, None) == 10
+    assert L.swiglu_mlp_infer_noalloc(*b, 1 << 20, D, H, 2, 0, None) == 10
+    assert L.swiglu_mlp_infer_noalloc(*b, 16, D, H, 0, 2, None) == 9        # flags
+    assert L.swiglu_mlp_infer_noalloc(*b[:4], b[0] + 64, 16, D, H, 0, 0, None) == 5  # Y overlaps X
