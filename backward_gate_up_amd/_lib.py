@@ -14,6 +14,7 @@ STATUS = {
 }
 NOALLOC_SCRATCH_BYTES = 32 << 20
 FLAG_TWO_ROUND = 1
+FLAG_LINEAR_WEIGHTS = 2
 NUM_STAGES = 10
 STAGE_NAMES = ("gateup_swiglu", "down_proj", "dgu_inplace", "dwd", "dwgu", "dx",
                "infer_gateup", "infer_down", "dwd+dgu", "dwgu+dx")
@@ -49,6 +50,8 @@ def lib():
     L.swiglu_mlp_fwd.restype = i32
     L.swiglu_mlp_bwd.argtypes = [vp] * 11 + [sz] + [i64] * 3 + [i32, vp]
     L.swiglu_mlp_bwd.restype = i32
+    L.swiglu_mlp_bwd_ex.argtypes = [vp] * 11 + [sz] + [i64] * 3 + [i32, ctypes.c_uint, vp]
+    L.swiglu_mlp_bwd_ex.restype = i32
     L.swiglu_mlp_infer.argtypes = [vp] * 6 + [sz] + [i64] * 3 + [i32, vp]
     L.swiglu_mlp_infer.restype = i32
     u32 = ctypes.c_uint

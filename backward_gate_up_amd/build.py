@@ -1,7 +1,8 @@
 """Build the HIP library in-tree: backward_gate_up_amd/libswiglu_mlp.so (gfx950).
 
-The kernels are instantiated in nine translation units (csrc/instantiate.hip
-compiled once per dtype and entry point) plus the C ABI (csrc/swiglu_mlp.hip);
+The kernels are instantiated in eighteen translation units (csrc/instantiate.hip
+compiled once per dtype, entry point and weight layout) plus the C ABI
+(csrc/swiglu_mlp.hip);
 they compile in parallel and are linked into one shared library.
 """
 
@@ -30,8 +31,10 @@ FLAGS = [
 
 # (object name, source, defines)
 UNITS = [("abi", "swiglu_mlp.hip", [])] + [
-    (f"{dt}_{op}", "instantiate.hip", [f"-DSWIGLU_INST_DTYPE={i}", f"-DSWIGLU_INST_OP={j}"])
+    (f"{dt}_{op}_{lay}", "instantiate.hip",
+     [f"-DSWIGLU_INST_DTYPE={i}", f"-DSWIGLU_INST_OP={j}", f"-DSWIGLU_INST_LIN={k}"])
     for i, dt in enumerate(("bf16", "fp16", "fp32")) for j, op in enumerate(("fwd", "bwd", "infer"))
+    for k, lay in enumerate(("kernel", "linear"))
 ]
 
 

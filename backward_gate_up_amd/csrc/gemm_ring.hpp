@@ -90,14 +90,18 @@ struct Dma {
   uint32_t voff[G::PPW];
 
   // Per-tile lane offsets. r0 is the first row (KC) or, for MC, unused here:
-  // MC sub-tiles are positioned through the descriptor.
-  __device__ __forceinline__ void init(const Operand& op, int r0, int wave, int lane) {
+  // MC sub-tiles are positioned through the descriptor. KC with `halves`:
+  // the tile's rows [0, 128) and [128, 256) are rows [r0, r0 + 128) of two
+  // operands of the same shape (waves 0-1 load the first, waves 2-3 the
+  // second; the caller passes each wave its operand).
+  __device__ __forceinline__ void init(const Operand& op, int r0, int wave, int lane, bool halves = false) {
 #pragma unroll
     for (int j = 0; j < G::PPW; ++j) {
       if constexpr (LAYOUT == KC) {
-        const int r = (wave * G::PPW + j) * G::RPI + lane / G::LPR;
+        const int r = (wave * G::PPW + j) * G::RPI + lane / G::LPR;  // row of the LDS tile
+        const int rr = halves ? (r & 127) : r;                       // row of the operand, from r0
         const int c = (lane % G::LPR) ^ kc_swz<BKT>(r);
-        voff[j] = (r0 + r < op.rows) ? (uint32_t)(r * (int)op.ld * 2 + c * 16) : kOOB;
+        voff[j] = (r0 + rr < op.rows) ? (uint32_t)(rr * (int)op.ld * 2 + c * 16) : kOOB;
       } else {
         const int kr = ((wave & 1) * G::PPW + j) * 4 + (lane >> 4);
         const int c = (lane & 15) ^ ((kr & 3) << 2);

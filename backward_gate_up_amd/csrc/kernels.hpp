@@ -55,6 +55,7 @@ struct KArgs {
   int tiles_m, tiles_n;
   int store_gu;    // GATEUP: write the G and U planes (training) or A only (no-grad)
   int planes;      // PLAIN: number of (B source, output) planes (1 or 2)
+  int plane_a;     // PLAIN, two planes: plane 1 takes its A operand from a1 (B shared) instead of B from b1
   int group_m;     // M-tiles per group of the tile walk (tile_coords); 0 = 8
   int two_round;   // GATEUP: A = rnd(rnd(SiLU(g)) * u) instead of rnd(SiLU(g) * u)
   float* P;        // PLAIN, split K: fp32 partial tiles, 256 x 256 each (else nullptr)
@@ -278,7 +279,8 @@ __device__ __forceinline__ void gemm_tile(const KArgs& g, char* smem, int bid, i
   Operand A = g.a0, B = g.b0;
   char* C = g.c0;
   if (KIND == PLAIN && bz == 1) {
-    B = g.b1;
+    if (g.plane_a) A = g.a1;
+    else B = g.b1;
     C = g.c1;
   }
 
@@ -630,7 +632,8 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   Operand A = g.a0, B = g.b0;
   char* C = g.c0;
   if (KIND == PLAIN && bz == 1) {
-    B = g.b1;
+    if (g.plane_a) A = g.a1;
+    else B = g.b1;
     C = g.c1;
   }
   int a_rows[4], b_rows[4];
@@ -649,7 +652,8 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   Dma<AL> da;
   Dma<BL> db;
   da.init(A, m0, wave, lane);
-  db.init(B, n0, wave, lane);
+  // gate/up with K-major weights: B rows [0, 128) from Wg, [128, 256) from Wu
+  db.init(B, n0, wave, lane, KIND == GATEUP && BL == KC);
   const int nk1 = (A.k + BK - 1) / BK;
   // split K (a piece of a weight-gradient tile): stages [sb, sb + nk) of
   // the K loop, written as fp32 partial tile `piece`
@@ -671,11 +675,14 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   auto issue_b = [&](int s, char* stg) {
     if constexpr (KIND == DX) {
       const bool h = s >= nk1;
-      db.issue_kc(h ? g.b1 : g.b0, n0, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
+      const Operand& op = h ? g.b1 : g.b0;
+      if constexpr (BL == KC) db.issue_kc(op, n0, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
+      else db.issue_mc(op, n0, op, n0 + 128, (h ? s - nk1 : s) * BK, stg + OPB, wave);
+    } else if constexpr (KIND == GATEUP) {
+      if constexpr (BL == KC) db.issue_kc(wave >= 2 ? g.b1 : g.b0, n0, s * BK, stg + OPB, wave, lane);
+      else db.issue_mc(g.b0, n0, g.b1, n0, s * BK, stg + OPB, wave);
     } else if constexpr (BL == KC) {
       db.issue_kc(B, n0, (sb + s) * BK, stg + OPB, wave, lane);
-    } else if constexpr (KIND == GATEUP) {
-      db.issue_mc(g.b0, n0, g.b1, n0, s * BK, stg + OPB, wave);
     } else {
       db.issue_mc(B, n0, B, n0 + 128, (sb + s) * BK, stg + OPB, wave);
     }
@@ -789,7 +796,8 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
   Operand A = g.a0, B = g.b0;
   char* C = g.c0;
   if (KIND == PLAIN && bz == 1) {
-    B = g.b1;
+    if (g.plane_a) A = g.a1;
+    else B = g.b1;
     C = g.c1;
   }
   int a_rows[4], b_rows[4];
@@ -808,7 +816,7 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
   Dma<AL, BK2> da;
   Dma<BL, BK2> db;
   da.init(A, m0, wave, lane);
-  db.init(B, n0, wave, lane);
+  db.init(B, n0, wave, lane, KIND == GATEUP && BL == KC);
   const int nk1 = (A.k + BK2 - 1) / BK2;
   const int nk = (KIND == DX) ? 2 * nk1 : nk1;
   constexpr int NT = Geo<BK2>::PPW;  // loads per wave per operand tile
@@ -827,11 +835,14 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
   auto issue_b = [&](int s, char* t) {
     if constexpr (KIND == DX) {
       const bool h = s >= nk1;
-      db.issue_kc(h ? g.b1 : g.b0, n0, (h ? s - nk1 : s) * BK2, t, wave, lane);
+      const Operand& op = h ? g.b1 : g.b0;
+      if constexpr (BL == KC) db.issue_kc(op, n0, (h ? s - nk1 : s) * BK2, t, wave, lane);
+      else db.issue_mc(op, n0, op, n0 + 128, (h ? s - nk1 : s) * BK2, t, wave);
+    } else if constexpr (KIND == GATEUP) {
+      if constexpr (BL == KC) db.issue_kc(wave >= 2 ? g.b1 : g.b0, n0, s * BK2, t, wave, lane);
+      else db.issue_mc(g.b0, n0, g.b1, n0, s * BK2, t, wave);
     } else if constexpr (BL == KC) {
       db.issue_kc(B, n0, s * BK2, t, wave, lane);
-    } else if constexpr (KIND == GATEUP) {
-      db.issue_mc(g.b0, n0, g.b1, n0, s * BK2, t, wave);
     } else {
       db.issue_mc(B, n0, B, n0 + 128, s * BK2, t, wave);
     }
@@ -1649,9 +1660,22 @@ static inline InferPlan infer_plan(int64_t T, int64_t D, int64_t H, size_t e) {
 // weight stream.
 static inline bool small_t(int64_t T) { return T <= 512; }
 
-template <class E>
+// The weights come in one of two layouts (the LIN template argument):
+//   kernel layout (LIN = false): Wg, Wu [D, H], Wd [H, D], row-major, so the
+//     forward reads them N-major and the backward (dA, dI) K-major;
+//   linear layout (LIN = true): the nn.Linear weights, gate_proj and
+//     up_proj [H, D], down_proj [D, H], row-major, so the forward reads them
+//     K-major and the backward N-major; the weight gradients are written in
+//     the same layout (dWg, dWu [H, D], dWd [D, H]).
+// Either way no weight is copied or transposed: each GEMM reads its operand
+// in the layout it is given (FW: the forward's weight operand layout, BW:
+// the backward's). The weight-streaming kernels assume N-contiguous weights,
+// so the linear layout runs few-token shapes on the 64-row tile engine.
+template <class E, bool LIN>
 struct Path {
   static constexpr int EB = E::kBytes;
+  static constexpr int FW = LIN ? KC : MC;
+  static constexpr int BW = LIN ? MC : KC;
 
   template <int STAGE>
   static int gateup(const void* X, const void* Wg, const void* Wu, char* Ap, char* Gp, char* Up,
@@ -1659,8 +1683,13 @@ struct Path {
                     hipStream_t s, unsigned* zero_ctr = nullptr, int n_zero = 0) {
     KArgs a{};
     a.a0 = opnd(X, D, T, D);
-    a.b0 = opnd(Wg, H, H, D);
-    a.b1 = opnd(Wu, H, H, D);
+    if constexpr (LIN) {
+      a.b0 = opnd(Wg, D, H, D);  // Bop[k=d][n=h] = Wg[h][d]: K-contiguous rows
+      a.b1 = opnd(Wu, D, H, D);
+    } else {
+      a.b0 = opnd(Wg, H, H, D);  // Bop[k=d][n=h] = Wg[d][h]: N-contiguous rows
+      a.b1 = opnd(Wu, H, H, D);
+    }
     a.c0 = Ap;
     a.c1 = Gp;
     a.c2 = Up;
@@ -1671,7 +1700,7 @@ struct Path {
     a.two_round = two_round ? 1 : 0;
     a.zero_ctr = zero_ctr;
     a.n_zero = n_zero;
-    if constexpr (E::kBytes == 2) {
+    if constexpr (E::kBytes == 2 && !LIN) {
       // (the streaming kernels are instantiated for the no-grad stage only)
       if constexpr (STAGE == 6)
         if (st) {
@@ -1683,12 +1712,12 @@ struct Path {
     if (small_t(T)) {
       a.tiles_m = cdiv(T, 64);
       a.tiles_n = cdiv(H, 128);
-      return launch<E, 64, 256, KC, MC, GATEUP, STAGE>(a, 1, s);
+      return launch<E, 64, 256, KC, FW, GATEUP, STAGE>(a, 1, s);
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(H, 128);
-    if constexpr (E::kBytes == 2) return launch_ring<E, KC, MC, GATEUP, STAGE>(a, 1, s);
-    else return launch<E, 256, 256, KC, MC, GATEUP, STAGE>(a, 1, s);
+    if constexpr (E::kBytes == 2) return launch_ring<E, KC, FW, GATEUP, STAGE>(a, 1, s);
+    else return launch<E, 256, 256, KC, FW, GATEUP, STAGE>(a, 1, s);
   }
 
   template <int STAGE>
@@ -1696,12 +1725,13 @@ struct Path {
                   const StreamArgs* st, hipStream_t s) {
     KArgs a{};
     a.a0 = opnd(Ap, H, T, H);
-    a.b0 = opnd(Wd, D, D, H);
+    if constexpr (LIN) a.b0 = opnd(Wd, H, D, H);  // Bop[k=h][n=d] = Wd[d][h]
+    else a.b0 = opnd(Wd, D, D, H);                // Bop[k=h][n=d] = Wd[h][d]
     a.c0 = (char*)Y;
     a.ldc = D;
     a.M = (int)T;
     a.N = (int)D;
-    if constexpr (E::kBytes == 2) {
+    if constexpr (E::kBytes == 2 && !LIN) {
       if constexpr (STAGE == 7)
         if (st) return launch_stream<E, PLAIN, STAGE>(a, T, D, *st, s);
       if (few_t(T)) return launch_skinny<E, PLAIN, STAGE>(a, T, D, s);
@@ -1712,26 +1742,27 @@ struct Path {
       a.tiles_m = cdiv(T, 64);
       if (a.tiles_m * cdiv(D, 256) >= 256) {
         a.tiles_n = cdiv(D, 256);
-        return launch<E, 64, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
+        return launch<E, 64, 256, KC, FW, PLAIN, STAGE>(a, 1, s);
       }
       if (a.tiles_m * cdiv(D, 128) >= 256) {
         a.tiles_n = cdiv(D, 128);
-        return launch<E, 64, 128, KC, MC, PLAIN, STAGE>(a, 1, s);
+        return launch<E, 64, 128, KC, FW, PLAIN, STAGE>(a, 1, s);
       }
       a.tiles_n = cdiv(D, 64);
-      return launch<E, 64, 64, KC, MC, PLAIN, STAGE>(a, 1, s);
+      return launch<E, 64, 64, KC, FW, PLAIN, STAGE>(a, 1, s);
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(D, 256);
-    if constexpr (E::kBytes == 2) return launch_ring<E, KC, MC, PLAIN, STAGE>(a, 1, s);
-    else return launch<E, 256, 256, KC, MC, PLAIN, STAGE>(a, 1, s);
+    if constexpr (E::kBytes == 2) return launch_ring<E, KC, FW, PLAIN, STAGE>(a, 1, s);
+    else return launch<E, 256, 256, KC, FW, PLAIN, STAGE>(a, 1, s);
   }
 
   // Backward stage arguments (tiles_m/tiles_n filled by the launchers).
   static KArgs args_dgu(const void* dY, const void* Wd, char* Gp, char* Up, int64_t T, int64_t D, int64_t H) {
     KArgs a{};
     a.a0 = opnd(dY, D, T, D);
-    a.b0 = opnd(Wd, D, H, D);  // Bop[k=d][n=h] = Wd[h][d]: K-contiguous rows of Wd
+    if constexpr (LIN) a.b0 = opnd(Wd, H, H, D);  // Bop[k=d][n=h] = Wd[d][h]: N-contiguous rows
+    else a.b0 = opnd(Wd, D, H, D);                // Bop[k=d][n=h] = Wd[h][d]: K-contiguous rows
     a.c0 = Gp;
     a.c1 = Up;
     a.ldc = H;
@@ -1742,30 +1773,52 @@ struct Path {
   }
   static KArgs args_dwd(const char* Ap, const void* dY, void* dWd, int64_t T, int64_t D, int64_t H) {
     KArgs a{};
-    a.a0 = opnd(Ap, H, H, T);  // Aop[m=h][k=t] = A[t][h]
-    a.b0 = opnd(dY, D, D, T);  // Bop[k=t][n=d] = dY[t][d]
+    if constexpr (LIN) {
+      // dWd [D, H] = dY^T A
+      a.a0 = opnd(dY, D, D, T);  // Aop[m=d][k=t] = dY[t][d]
+      a.b0 = opnd(Ap, H, H, T);  // Bop[k=t][n=h] = A[t][h]
+      a.ldc = H;
+      a.M = (int)D;
+      a.N = (int)H;
+    } else {
+      // dWd [H, D] = A^T dY
+      a.a0 = opnd(Ap, H, H, T);  // Aop[m=h][k=t] = A[t][h]
+      a.b0 = opnd(dY, D, D, T);  // Bop[k=t][n=d] = dY[t][d]
+      a.ldc = D;
+      a.M = (int)H;
+      a.N = (int)D;
+    }
     a.c0 = (char*)dWd;
-    a.ldc = D;
-    a.M = (int)H;
-    a.N = (int)D;
-    a.tiles_m = cdiv(H, 256);
-    a.tiles_n = cdiv(D, 256);
+    a.tiles_m = cdiv(a.M, 256);
+    a.tiles_n = cdiv(a.N, 256);
     a.planes = 1;
     return a;
   }
   static KArgs args_dwgu(const void* X, const char* dGp, const char* dUp, void* dWg, void* dWu, int64_t T,
                          int64_t D, int64_t H) {
     KArgs a{};
-    a.a0 = opnd(X, D, D, T);    // Aop[m=d][k=t] = X[t][d]
-    a.b0 = opnd(dGp, H, H, T);  // Bop[k=t][n=h] = dG[t][h]
-    a.b1 = opnd(dUp, H, H, T);
+    if constexpr (LIN) {
+      // dWg, dWu [H, D] = dG^T X, dU^T X: the planes switch the A operand
+      a.a0 = opnd(dGp, H, H, T);  // Aop[m=h][k=t] = dG[t][h]
+      a.a1 = opnd(dUp, H, H, T);
+      a.b0 = opnd(X, D, D, T);    // Bop[k=t][n=d] = X[t][d]
+      a.plane_a = 1;
+      a.ldc = D;
+      a.M = (int)H;
+      a.N = (int)D;
+    } else {
+      // [dWg | dWu] [D, H] = X^T [dG | dU]: the planes switch the B operand
+      a.a0 = opnd(X, D, D, T);    // Aop[m=d][k=t] = X[t][d]
+      a.b0 = opnd(dGp, H, H, T);  // Bop[k=t][n=h] = dG[t][h]
+      a.b1 = opnd(dUp, H, H, T);
+      a.ldc = H;
+      a.M = (int)D;
+      a.N = (int)H;
+    }
     a.c0 = (char*)dWg;
     a.c1 = (char*)dWu;
-    a.ldc = H;
-    a.M = (int)D;
-    a.N = (int)H;
-    a.tiles_m = cdiv(D, 256);
-    a.tiles_n = cdiv(H, 256);
+    a.tiles_m = cdiv(a.M, 256);
+    a.tiles_n = cdiv(a.N, 256);
     a.planes = 2;
     return a;
   }
@@ -1774,8 +1827,13 @@ struct Path {
     KArgs a{};
     a.a0 = opnd(dGp, H, T, H);
     a.a1 = opnd(dUp, H, T, H);
-    a.b0 = opnd(Wg, H, D, H);  // Bop[k=h][n=d] = Wg[d][h]: K-contiguous rows of Wg
-    a.b1 = opnd(Wu, H, D, H);
+    if constexpr (LIN) {
+      a.b0 = opnd(Wg, D, D, H);  // Bop[k=h][n=d] = Wg[h][d]: N-contiguous rows
+      a.b1 = opnd(Wu, D, D, H);
+    } else {
+      a.b0 = opnd(Wg, H, D, H);  // Bop[k=h][n=d] = Wg[d][h]: K-contiguous rows
+      a.b1 = opnd(Wu, H, D, H);
+    }
     a.c0 = (char*)dX;
     a.ldc = D;
     a.M = (int)T;
@@ -1791,11 +1849,11 @@ struct Path {
     if (small_t(T)) {
       dgu.tiles_m = cdiv(T, 64);
       dgu.tiles_n = cdiv(H, 256);
-      rc = launch<E, 64, 256, KC, KC, DSWIGLU, 2>(dgu, 1, s);
+      rc = launch<E, 64, 256, KC, BW, DSWIGLU, 2>(dgu, 1, s);
     } else {
       dgu.tiles_m = cdiv(T, 256);
       dgu.tiles_n = cdiv(H, 256);
-      rc = launch<E, 256, 256, KC, KC, DSWIGLU, 2>(dgu, 1, s);
+      rc = launch<E, 256, 256, KC, BW, DSWIGLU, 2>(dgu, 1, s);
     }
     if (rc) return rc;
     if ((rc = launch<E, 256, 256, MC, MC, PLAIN, 3>(dwd, 1, s))) return rc;
@@ -1803,11 +1861,11 @@ struct Path {
     if (small_t(T)) {
       dx.tiles_m = cdiv(T, 64);
       dx.tiles_n = cdiv(D, 256);
-      return launch<E, 64, 256, KC, KC, DX, 5>(dx, 1, s);
+      return launch<E, 64, 256, KC, BW, DX, 5>(dx, 1, s);
     }
     dx.tiles_m = cdiv(T, 256);
     dx.tiles_n = cdiv(D, 256);
-    return launch<E, 256, 256, KC, KC, DX, 5>(dx, 1, s);
+    return launch<E, 256, 256, KC, BW, DX, 5>(dx, 1, s);
   }
 
   // T > 512. bf16/fp16: the four ring launches (stages 2, 3, 4, 5). fp32 on
@@ -1823,62 +1881,63 @@ struct Path {
       // one ring launch per step: measured 0.5 % faster than pairing the
       // short-K stages with the long-K weight gradients on the ring engine
       int rc;
-      if ((rc = launch_ring<E, KC, KC, DSWIGLU, 2>(dgu, 1, s))) return rc;
+      if ((rc = launch_ring<E, KC, BW, DSWIGLU, 2>(dgu, 1, s))) return rc;
       if ((rc = launch_ring_wgrad<E, MC, MC, 3>(dwd, 1, P, s))) return rc;
       if ((rc = launch_ring_wgrad<E, MC, MC, 4>(dwgu, 2, P, s))) return rc;
-      return launch_ring<E, KC, KC, DX, 5>(dx, 1, s);
+      return launch_ring<E, KC, BW, DX, 5>(dx, 1, s);
     } else {
-      int rc = launch_pair<E, MC, MC, PLAIN, KC, KC, DSWIGLU, 8>(dwd, dgu, s);
+      int rc = launch_pair<E, MC, MC, PLAIN, KC, BW, DSWIGLU, 8>(dwd, dgu, s);
       if (rc) return rc;
-      return launch_pair<E, MC, MC, PLAIN, KC, KC, DX, 9>(dwgu, dx, s);
+      return launch_pair<E, MC, MC, PLAIN, KC, BW, DX, 9>(dwgu, dx, s);
     }
   }
 };
 
-template <class E>
+template <class E, bool LIN>
 int run_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
-                   int64_t D, int64_t H, bool two_round, hipStream_t s) {
+            int64_t D, int64_t H, bool two_round, hipStream_t s) {
   const size_t plane = (size_t)T * H * E::kBytes;
   char* Ap = (char*)saved;
-  int rc = Path<E>::template gateup<0>(X, Wg, Wu, Ap, Ap + plane, Ap + 2 * plane, T, D, H, true, two_round,
-                                       nullptr, s);
+  int rc = Path<E, LIN>::template gateup<0>(X, Wg, Wu, Ap, Ap + plane, Ap + 2 * plane, T, D, H, true, two_round,
+                                            nullptr, s);
   if (rc) return rc;
-  return Path<E>::template down<1>(Ap, Wd, Y, T, D, H, nullptr, s);
+  return Path<E, LIN>::template down<1>(Ap, Wd, Y, T, D, H, nullptr, s);
 }
 
-template <class E>
-int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
-                   void* dX, void* dWg, void* dWu, void* dWd, float* P, int64_t T, int64_t D, int64_t H,
-                   hipStream_t s) {
+template <class E, bool LIN>
+int run_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved, void* dX,
+            void* dWg, void* dWu, void* dWd, float* P, int64_t T, int64_t D, int64_t H, hipStream_t s) {
+  using Pa = Path<E, LIN>;
   const size_t plane = (size_t)T * H * E::kBytes;
   char* Ap = (char*)saved;
   char* Gp = Ap + plane;
   char* Up = Ap + 2 * plane;
-  KArgs dgu = Path<E>::args_dgu(dY, Wd, Gp, Up, T, D, H);
-  KArgs dwd = Path<E>::args_dwd(Ap, dY, dWd, T, D, H);
-  KArgs dwgu = Path<E>::args_dwgu(X, Gp, Up, dWg, dWu, T, D, H);
-  KArgs dx = Path<E>::args_dx(Gp, Up, Wg, Wu, dX, T, D, H);
-  if (small_t(T)) return Path<E>::bwd_separate(dgu, dwd, dwgu, dx, T, D, H, s);
-  return Path<E>::bwd_large(dgu, dwd, dwgu, dx, T, D, H, P, s);
+  KArgs dgu = Pa::args_dgu(dY, Wd, Gp, Up, T, D, H);
+  KArgs dwd = Pa::args_dwd(Ap, dY, dWd, T, D, H);
+  KArgs dwgu = Pa::args_dwgu(X, Gp, Up, dWg, dWu, T, D, H);
+  KArgs dx = Pa::args_dx(Gp, Up, Wg, Wu, dX, T, D, H);
+  if (small_t(T)) return Pa::bwd_separate(dgu, dwd, dwgu, dx, T, D, H, s);
+  return Pa::bwd_large(dgu, dwd, dwgu, dx, T, D, H, P, s);
 }
 
-template <class E>
+template <class E, bool LIN>
 int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws, int64_t T,
               int64_t D, int64_t H, bool two_round, hipStream_t s) {
+  using Pa = Path<E, LIN>;
   char* Ap = (char*)ws;
   const InferPlan pl = infer_plan(T, D, H, E::kBytes);
-  if (pl.down_units == 0) {
-    int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, nullptr, s);
+  if (LIN || pl.down_units == 0) {
+    int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, nullptr, s);
     if (rc) return rc;
-    return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, nullptr, s);
+    return Pa::template down<7>(Ap, Wd, Y, T, D, H, nullptr, s);
   }
   unsigned* ctr = (unsigned*)(Ap + pl.ctr_off);
   const StreamArgs sg{1, nullptr, nullptr};
   const StreamArgs sd{pl.down_splits, pl.down_splits > 1 ? (float*)(Ap + pl.p_off) : nullptr, ctr};
-  int rc = Path<E>::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, &sg, s, ctr,
-                                       pl.down_units);
+  int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, &sg, s, ctr,
+                                  pl.down_units);
   if (rc) return rc;
-  return Path<E>::template down<7>(Ap, Wd, Y, T, D, H, &sd, s);
+  return Pa::template down<7>(Ap, Wd, Y, T, D, H, &sd, s);
 }
 
 }  // namespace swiglu

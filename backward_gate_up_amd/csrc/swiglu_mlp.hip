@@ -10,17 +10,50 @@ namespace swiglu {
 Timer g_timer;
 
 // the drivers are compiled in their own translation units (instantiate.hip)
-#define SWIGLU_DECLARE_DRIVERS(E)                                                                                 \
-  extern template int run_fwd<E>(const void*, const void*, const void*, const void*, void*, void*, int64_t,       \
-                                 int64_t, int64_t, bool, hipStream_t);                                            \
-  extern template int run_bwd<E>(const void*, const void*, const void*, const void*, const void*, void*, void*,   \
-                                 void*, void*, void*, float*, int64_t, int64_t, int64_t, hipStream_t);            \
-  extern template int run_infer<E>(const void*, const void*, const void*, const void*, void*, void*, int64_t,     \
-                                   int64_t, int64_t, bool, hipStream_t);
-SWIGLU_DECLARE_DRIVERS(Bf16)
-SWIGLU_DECLARE_DRIVERS(Fp16)
-SWIGLU_DECLARE_DRIVERS(Fp32)
+#define SWIGLU_DECLARE_DRIVERS(E, LIN)                                                                            \
+  extern template int run_fwd<E, LIN>(const void*, const void*, const void*, const void*, void*, void*, int64_t,  \
+                                      int64_t, int64_t, bool, hipStream_t);                                       \
+  extern template int run_bwd<E, LIN>(const void*, const void*, const void*, const void*, const void*, void*,     \
+                                      void*, void*, void*, void*, float*, int64_t, int64_t, int64_t, hipStream_t); \
+  extern template int run_infer<E, LIN>(const void*, const void*, const void*, const void*, void*, void*,         \
+                                        int64_t, int64_t, int64_t, bool, hipStream_t);
+SWIGLU_DECLARE_DRIVERS(Bf16, false)
+SWIGLU_DECLARE_DRIVERS(Fp16, false)
+SWIGLU_DECLARE_DRIVERS(Fp32, false)
+SWIGLU_DECLARE_DRIVERS(Bf16, true)
+SWIGLU_DECLARE_DRIVERS(Fp16, true)
+SWIGLU_DECLARE_DRIVERS(Fp32, true)
 #undef SWIGLU_DECLARE_DRIVERS
+
+// The driver for a dtype code and weight layout.
+template <bool LIN>
+static int fwd_for(int dtype, const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved,
+                   int64_t T, int64_t D, int64_t H, bool two_round, hipStream_t s) {
+  switch (dtype) {
+    case SWIGLU_BF16: return run_fwd<Bf16, LIN>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, s);
+    case SWIGLU_FP16: return run_fwd<Fp16, LIN>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, s);
+    default: return run_fwd<Fp32, LIN>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, s);
+  }
+}
+template <bool LIN>
+static int bwd_for(int dtype, const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd,
+                   void* saved, void* dX, void* dWg, void* dWu, void* dWd, float* P, int64_t T, int64_t D, int64_t H,
+                   hipStream_t s) {
+  switch (dtype) {
+    case SWIGLU_BF16: return run_bwd<Bf16, LIN>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, P, T, D, H, s);
+    case SWIGLU_FP16: return run_bwd<Fp16, LIN>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, P, T, D, H, s);
+    default: return run_bwd<Fp32, LIN>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, nullptr, T, D, H, s);
+  }
+}
+template <bool LIN>
+static int infer_for(int dtype, const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws,
+                     int64_t T, int64_t D, int64_t H, bool two_round, hipStream_t s) {
+  switch (dtype) {
+    case SWIGLU_BF16: return run_infer<Bf16, LIN>(X, Wg, Wu, Wd, Y, ws, T, D, H, two_round, s);
+    case SWIGLU_FP16: return run_infer<Fp16, LIN>(X, Wg, Wu, Wd, Y, ws, T, D, H, two_round, s);
+    default: return run_infer<Fp32, LIN>(X, Wg, Wu, Wd, Y, ws, T, D, H, two_round, s);
+  }
+}
 
 // Fill kernel (used to clear weight gradients when T = 0 would otherwise
 // leave them unwritten; a kernel rather than a memset so that callers may
@@ -161,11 +194,9 @@ int swiglu_mlp_fwd_ex(const void* X, const void* Wg, const void* Wu, const void*
   if (overlap(out[0], out[1])) return SWIGLU_ERR_ALIAS;
   if ((rc = check_device())) return rc;
   if (T == 0) return SWIGLU_OK;
-  switch (dtype) {
-    case SWIGLU_BF16: return run_fwd<Bf16>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
-    case SWIGLU_FP16: return run_fwd<Fp16>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
-    default: return run_fwd<Fp32>(X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
-  }
+  if (flags & SWIGLU_FLAG_LINEAR_WEIGHTS)
+    return fwd_for<true>(dtype, X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
+  return fwd_for<false>(dtype, X, Wg, Wu, Wd, Y, saved, T, D, H, two_round, stream);
 }
 
 int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* saved, int64_t T,
@@ -173,11 +204,12 @@ int swiglu_mlp_fwd(const void* X, const void* Wg, const void* Wu, const void* Wd
   return swiglu_mlp_fwd_ex(X, Wg, Wu, Wd, Y, saved, T, D, H, dtype, 0u, stream);
 }
 
-int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
-                   void* dX, void* dWg, void* dWu, void* dWd, void* workspace, size_t workspace_bytes, int64_t T,
-                   int64_t D, int64_t H, int dtype, hipStream_t stream) {
+int swiglu_mlp_bwd_ex(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
+                      void* dX, void* dWg, void* dWu, void* dWd, void* workspace, size_t workspace_bytes, int64_t T,
+                      int64_t D, int64_t H, int dtype, unsigned flags, hipStream_t stream) {
   size_t e = elt_bytes(dtype);
   if (!e) return SWIGLU_ERR_DTYPE;
+  if (flags & ~SWIGLU_FLAGS_ALL) return SWIGLU_ERR_FLAGS;
   int rc = check_shape(T, D, H, e);
   if (rc) return rc;
   const size_t td = (size_t)T * D * e, dh = (size_t)D * H * e;
@@ -200,14 +232,16 @@ int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
     if ((rc = zero_fill(dWu, dh, stream))) return rc;
     return zero_fill(dWd, dh, stream);
   }
-  switch (dtype) {
-    case SWIGLU_BF16:
-      return run_bwd<Bf16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, (float*)workspace, T, D, H, stream);
-    case SWIGLU_FP16:
-      return run_bwd<Fp16>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, (float*)workspace, T, D, H, stream);
-    default:
-      return run_bwd<Fp32>(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, nullptr, T, D, H, stream);
-  }
+  if (flags & SWIGLU_FLAG_LINEAR_WEIGHTS)
+    return bwd_for<true>(dtype, dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, (float*)workspace, T, D, H, stream);
+  return bwd_for<false>(dtype, dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, (float*)workspace, T, D, H, stream);
+}
+
+int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu, const void* Wd, void* saved,
+                   void* dX, void* dWg, void* dWu, void* dWd, void* workspace, size_t workspace_bytes, int64_t T,
+                   int64_t D, int64_t H, int dtype, hipStream_t stream) {
+  return swiglu_mlp_bwd_ex(dY, X, Wg, Wu, Wd, saved, dX, dWg, dWu, dWd, workspace, workspace_bytes, T, D, H, dtype,
+                           0u, stream);
 }
 
 int swiglu_mlp_infer_ex(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* workspace,
@@ -232,11 +266,9 @@ int swiglu_mlp_infer_ex(const void* X, const void* Wg, const void* Wu, const voi
   if (overlap(out[0], out[1])) return SWIGLU_ERR_ALIAS;
   if ((rc = check_device())) return rc;
   if (T == 0) return SWIGLU_OK;
-  switch (dtype) {
-    case SWIGLU_BF16: return run_infer<Bf16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
-    case SWIGLU_FP16: return run_infer<Fp16>(X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
-    default: return run_infer<Fp32>(X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
-  }
+  if (flags & SWIGLU_FLAG_LINEAR_WEIGHTS)
+    return infer_for<true>(dtype, X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
+  return infer_for<false>(dtype, X, Wg, Wu, Wd, Y, workspace, T, D, H, two_round, stream);
 }
 
 int swiglu_mlp_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y, void* workspace,

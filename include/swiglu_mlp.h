@@ -78,7 +78,9 @@ typedef enum {
   SWIGLU_ERR_SCRATCH = 10   /* swiglu_mlp_infer_noalloc: the call needs more than its fixed scratch */
 } swiglu_status_t;
 
-/* Flags of swiglu_mlp_fwd_ex / swiglu_mlp_infer_ex.
+/* Flags of the _ex entry points (swiglu_mlp_fwd_ex, swiglu_mlp_bwd_ex,
+ * swiglu_mlp_infer_ex, swiglu_mlp_infer_noalloc).
+ *
  * SWIGLU_FLAG_TWO_ROUND selects the historical two-round SwiGLU program of
  * "Scope one-round FP32 SwiGLU to the exact Qwen3.5 contract" (xorl PR #51,
  * review thread): A = rnd(rnd(SiLU(g)) * u), SiLU(g) rounded to the storage
@@ -86,9 +88,22 @@ typedef enum {
  * pipelines that store SiLU(g) first. The page reports that about 27% of
  * bf16 outputs differ from the one-round program. Only A changes: G, U and
  * the backward are as without the flag, and the backward's dWd uses the A it
- * finds in the saved buffer. In SWIGLU_FP32 the two programs coincide. */
+ * finds in the saved buffer (the backward ignores the flag). In SWIGLU_FP32
+ * the two programs coincide.
+ *
+ * SWIGLU_FLAG_LINEAR_WEIGHTS: the weights (and the weight gradients the
+ * backward writes) are in the layout of the nn.Linear layers of the
+ * transformers MLP modules ("an interchangeable layer which has identical
+ * __init__ and forward signatures as hf/transformers xxxMLP", maintainers'
+ * thread on the mirror of issue #1347, "Three levels of APIs"):
+ * Wg = gate_proj.weight and Wu = up_proj.weight are [H, D], Wd =
+ * down_proj.weight is [D, H], all row-major; dWg, dWu are then [H, D] and
+ * dWd is [D, H]. The kernels read this layout directly (no transposed
+ * copy). The forward, backward and no-grad call of one computation must
+ * all pass the same layout flag. */
 #define SWIGLU_FLAG_TWO_ROUND 1u
-#define SWIGLU_FLAGS_ALL 1u
+#define SWIGLU_FLAG_LINEAR_WEIGHTS 2u
+#define SWIGLU_FLAGS_ALL 3u
 
 /* Bytes of the saved A|G|U buffer: 3 * T * H * sizeof(dtype). 0 on bad args. */
 size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
@@ -100,7 +115,9 @@ size_t swiglu_mlp_saved_bytes(int64_t T, int64_t H, int dtype);
  * 256-byte aligned, one arrival counter per 64 columns of the down
  * projection and the fp32 partial sums of its K splits, capped so that
  * workspace + Y stays within 3 (A + Y) (D = 4096, H = 11008, T = 128:
- * 10.2 MB against A + Y = 3.9 MB). 0 on bad args. */
+ * 10.2 MB against A + Y = 3.9 MB). The size covers both weight layouts
+ * (with SWIGLU_FLAG_LINEAR_WEIGHTS only the A plane is used). 0 on bad
+ * args. */
 size_t swiglu_mlp_infer_workspace_bytes(int64_t T, int64_t D, int64_t H, int dtype);
 
 /* Bytes of the backward workspace: fp32 partial tiles (256 x 256, 256 KiB
@@ -137,6 +154,16 @@ int swiglu_mlp_bwd(const void* dY, const void* X, const void* Wg, const void* Wu
                    const void* Wd, void* saved, void* dX, void* dWg, void* dWu,
                    void* dWd, void* workspace, size_t workspace_bytes,
                    int64_t T, int64_t D, int64_t H, int dtype, hipStream_t stream);
+
+/* swiglu_mlp_bwd with flags (SWIGLU_FLAG_*); flags = 0 is swiglu_mlp_bwd.
+ * With SWIGLU_FLAG_LINEAR_WEIGHTS the weights are read, and dWg, dWu, dWd
+ * written, in the nn.Linear layout. Unknown bits: SWIGLU_ERR_FLAGS, nothing
+ * launched. */
+int swiglu_mlp_bwd_ex(const void* dY, const void* X, const void* Wg, const void* Wu,
+                      const void* Wd, void* saved, void* dX, void* dWg, void* dWu,
+                      void* dWd, void* workspace, size_t workspace_bytes,
+                      int64_t T, int64_t D, int64_t H, int dtype, unsigned flags,
+                      hipStream_t stream);
 
 /* No-grad forward: Y [T, D] from X and the weights; G and U are never
  * stored. workspace (>= swiglu_mlp_infer_workspace_bytes bytes) holds A and,

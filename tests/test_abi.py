@@ -134,11 +134,14 @@ def test_no_device_is_reported_not_crashed():
 def test_unknown_flags_rejected_before_anything_else():
     L = _lib()
     b = [BASE + (i << 30) for i in range(7)]
-    for bad in (2, 4, 0x80000000):
+    for bad in (4, 8, 0x80000000):
         assert L.swiglu_mlp_fwd_ex(*b[:6], 16, 64, 128, 0, bad, None) == 9
         assert L.swiglu_mlp_infer_ex(*b[:6], 16 * 128 * 2, 16, 64, 128, 0, bad, None) == 9
+        assert L.swiglu_mlp_bwd_ex(*[b[i % 7] + (i << 34) for i in range(10)], None, 0, 16, 64, 128, 0, bad,
+                                   None) == 9
     # a bad dtype is reported first; known flags pass to the remaining checks
-    assert L.swiglu_mlp_fwd_ex(*b[:6], 16, 64, 128, 7, 2, None) == 3
+    assert L.swiglu_mlp_fwd_ex(*b[:6], 16, 64, 128, 7, 4, None) == 3
+    assert L.swiglu_mlp_fwd_ex(b[0], b[1], b[2], b[3], b[0] + 64, b[5], 16, 64, 128, 0, 3, None) == 5
     assert L.swiglu_mlp_fwd_ex(b[0], b[1], b[2], b[3], b[0] + 64, b[5], 16, 64, 128, 0, 1, None) == 5
     assert L.swiglu_mlp_infer_ex(*b[:5], None, 0, 16, 64, 128, 0, 1, None) == 6
 
@@ -200,5 +203,5 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     assert L.swiglu_mlp_infer_workspace_bytes(1525, D, H, 0) > NOALLOC_SCRATCH_BYTES
     assert L.swiglu_mlp_infer_noalloc(*b, 1525, D, H, 0, 0, None) == 10
     assert L.swiglu_mlp_infer_noalloc(*b, 1 << 20, D, H, 2, 0, None) == 10
-    assert L.swiglu_mlp_infer_noalloc(*b, 16, D, H, 0, 2, None) == 9        # flags
+    assert L.swiglu_mlp_infer_noalloc(*b, 16, D, H, 0, 4, None) == 9        # flags
     assert L.swiglu_mlp_infer_noalloc(*b[:4], b[0] + 64, 16, D, H, 0, 0, None) == 5  # Y overlaps X

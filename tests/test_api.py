@@ -50,19 +50,62 @@ def test_caller_buffers_checked():
 
 
 def test_module_layout_and_from_linears():
-    mod = m.SwiGLUMLP(64, 128, dtype=torch.bfloat16, generator=torch.Generator().manual_seed(1))
+    mod = m.SwiGLUMLPPacked(64, 128, dtype=torch.bfloat16, generator=torch.Generator().manual_seed(1))
     assert (mod.hidden_size, mod.intermediate_size) == (64, 128)
     assert mod.w_gate.shape == (64, 128) and mod.w_up.shape == (64, 128) and mod.w_down.shape == (128, 64)
     assert len(list(mod.parameters())) == 3
     lin = [torch.nn.Linear(64, 128, bias=False), torch.nn.Linear(64, 128, bias=False),
            torch.nn.Linear(128, 64, bias=False)]
-    m2 = m.SwiGLUMLP.from_linears(*lin)
+    m2 = m.SwiGLUMLPPacked.from_linears(*lin)
     # x @ W.T for nn.Linear equals x @ w in the kernels' layout
     assert torch.equal(m2.w_gate, lin[0].weight.t())
     assert torch.equal(m2.w_up, lin[1].weight.t())
     assert torch.equal(m2.w_down, lin[2].weight.t())
     assert m2.w_gate.is_contiguous() and m2.w_down.is_contiguous()
     with pytest.raises(ValueError, match="bias"):
-        m.SwiGLUMLP.from_linears(torch.nn.Linear(64, 128), *lin[1:])
+        m.SwiGLUMLPPacked.from_linears(torch.nn.Linear(64, 128), *lin[1:])
     with pytest.raises(ValueError, match="GPU"):
         mod(torch.randn(2, 3, 64).to(torch.bfloat16))
+
+
+def test_hf_interchangeable_module_matches_llama_mlp_surface():
+    """SwiGLUMLP(config) has LlamaMLP's constructor, attributes, submodules
+    and state-dict keys and shapes (nn.Linear layout), so a LlamaMLP state
+    dict loads unchanged, strictly; bias and non-SiLU activations are
+    refused."""
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaMLP
+
+    cfg = LlamaConfig(hidden_size=64, intermediate_size=160)
+    ref = LlamaMLP(cfg)
+    mod = m.SwiGLUMLP(cfg)
+    assert (mod.hidden_size, mod.intermediate_size) == (64, 160) and mod.config is cfg
+    sd = ref.state_dict()
+    assert {k: tuple(v.shape) for k, v in mod.state_dict().items()} == {k: tuple(v.shape) for k, v in sd.items()}
+    mod.load_state_dict(sd, strict=True)
+    for name in ("gate_proj", "up_proj", "down_proj"):
+        assert torch.equal(getattr(mod, name).weight, getattr(ref, name).weight)
+        assert getattr(mod, name).bias is None
+    import inspect
+    assert list(inspect.signature(mod.forward).parameters) == list(inspect.signature(ref.forward).parameters)
+    with pytest.raises(ValueError, match="bias"):
+        m.SwiGLUMLP(LlamaConfig(hidden_size=64, intermediate_size=160, mlp_bias=True))
+    with pytest.raises(ValueError, match="hidden_act"):
+        m.SwiGLUMLP(LlamaConfig(hidden_size=64, intermediate_size=160, hidden_act="gelu"))
+    with pytest.raises(ValueError, match="GPU"):
+        mod.to(torch.bfloat16)(torch.randn(2, 3, 64).to(torch.bfloat16))
+
+
+def test_linear_layout_shape_checks():
+    x = torch.empty(4, 64, dtype=torch.bfloat16)
+    wk = (torch.empty(64, 96, dtype=torch.bfloat16), torch.empty(64, 96, dtype=torch.bfloat16),
+          torch.empty(96, 64, dtype=torch.bfloat16))
+    wl = tuple(w.t().contiguous() for w in wk)
+    with pytest.raises(ValueError, match="GPU"):
+        m._shapes(x, *wk)
+    with pytest.raises(ValueError, match="GPU"):
+        m._shapes(x, *wl, linear=True)
+    with pytest.raises(ValueError, match="shape mismatch"):
+        m._shapes(x, *wk, linear=True)
+    with pytest.raises(ValueError, match="shape mismatch"):
+        m._shapes(x, *wl)
