@@ -1382,6 +1382,204 @@ __global__ void __launch_bounds__(256) stream_gemm(const KArgs g, float* P, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight streaming with a workgroup-shared ring, no-grad forward with
+// 32 < T <= 256 (MT = 4, 8 or 16 token tiles of 16). The per-wave ring of
+// stream_gemm holds each wave's own activation tiles, so with many tokens
+// only two slots fit and every step waits on its own loads. Here one stage
+// (32 K) is the unit's weight slabs (NW x 4 KiB) and the activation tiles
+// (MT KiB), loaded once for the workgroup and read by all four waves, which
+// split the 64 columns x MT token tiles 2 x 2; NSTG stages (6 or 8) are in
+// flight. Each wave then owns whole outputs: splits == 1 applies the
+// epilogue from registers, splits > 1 writes partials and counts arrivals
+// as stream_gemm does.
+// ---------------------------------------------------------------------------
+template <int KIND, int MT>
+struct RingStreamCfg {
+  static constexpr int NW = KIND == GATEUP ? 2 : 1;
+  static constexpr int C = NW * 4 + MT;  // 1-KiB loads per stage (= KiB per stage)
+  static_assert(C % 4 == 0, "every wave issues the same number of loads");
+  static constexpr int LW = C / 4;        // loads per wave per stage
+  static constexpr int NSTG = 160 / C > 8 ? 8 : 160 / C;
+  static constexpr int BYTES = NSTG * C * 1024;
+};
+
+template <class E, int KIND, int MT>
+__global__ void __launch_bounds__(256) stream_ring(const KArgs g, float* P, int splits, unsigned* ctr) {
+  using namespace stream;
+  using skinny::act_frag;
+  using skinny::mfma16;
+  using Cfg = RingStreamCfg<KIND, MT>;
+  constexpr int NW = Cfg::NW, C = Cfg::C, LW = Cfg::LW, NSTG = Cfg::NSTG;
+  constexpr int SLOT = C * 1024;
+  constexpr int TW = MT / 2;  // token tiles per wave
+  static_assert(MT >= 2 && MT % 2 == 0, "two token halves");
+  static_assert(Cfg::BYTES <= 160 * 1024, "LDS");
+  static_assert((NSTG - 2) * LW <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ch = wave & 1, th = wave >> 1;  // column half (32 columns), token half (TW tiles)
+  const int unit = blockIdx.x / splits, split = blockIdx.x - unit * splits;
+  if constexpr (KIND == GATEUP) clear_counters(g);
+  const int n0 = unit * NC;
+  const Operand& X = g.a0;
+  const int K = X.k, N = g.N, T = g.M;
+  const int steps = (K + KS - 1) / KS;
+  const int psplit = (steps + splits - 1) / splits;
+  const int s0 = split * psplit;
+  const int s1 = s0 + psplit < steps ? s0 + psplit : steps;
+  const int nst = s1 > s0 ? s1 - s0 : 0;
+
+  const uint32_t ring_addr = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  const int64_t ldw = g.b0.ld;
+  const char* wb1 = NW == 2 ? g.b1.base : g.b0.base;
+  // T <= 256 rows of at most 4194296 elements: every offset below 2^31
+  const i32x4_t rx = rsrc_words(X.base, (int64_t)X.rows * X.ld * 2);
+  // This wave's loads of a stage: load q = wave * LW + j of the C loads;
+  // q < NW * 4: weight slab q / 4, rows 8 (q % 4) .. + 7 (lane -> row
+  // 8 (q % 4) + lane / 8, physical chunk lane % 8 holding logical chunk
+  // (lane % 8) ^ wswz(row)); else activation tile q - NW * 4 (lane ->
+  // token row lane / 4 of the tile, logical chunk of its slot).
+  uint32_t voff[LW];
+  int kind[LW];  // 0, 1: weight plane; 2: activation
+  const int am = lane >> 2;
+  const int ac = (lane & 3) ^ ((am >> 2) & 3);
+#pragma unroll
+  for (int j = 0; j < LW; ++j) {
+    const int q = wave * LW + j;
+    if (q < NW * 4) {
+      const int row = (q & 3) * 8 + (lane >> 3);
+      const int col = n0 + (((lane & 7) ^ wswz(row)) << 3);
+      kind[j] = q >> 2;
+      voff[j] = col < N ? (uint32_t)row * (uint32_t)ldw * 2u + (uint32_t)col * 2u : kOOB;
+    } else {
+      const int m = (q - NW * 4) * 16 + am;
+      kind[j] = 2;
+      voff[j] = m < T ? (uint32_t)m * (uint32_t)X.ld * 2u + (uint32_t)ac * 16u : kOOB;
+    }
+  }
+
+  // loads of stage i (K rows [k0, k0 + 32)) into slot sl; past the end they
+  // fetch nothing (out-of-range offsets: zeros) and only keep the counts
+  auto issue = [&](int i, int sl) {
+    const bool live = i < nst;
+    const int k0 = (s0 + i) * KS;
+    const int kk = live ? k0 : 0;
+    const uint32_t base = ring_addr + sl * SLOT;
+    // weight descriptors from K row k0 to K: rows of a ragged last stage
+    // past K read as zeros
+    const int64_t wbytes = (int64_t)(K - kk) * ldw * 2;
+    const i32x4_t r0 = rsrc_words(g.b0.base + (int64_t)kk * ldw * 2, wbytes);
+    const i32x4_t r1 = rsrc_words(wb1 + (int64_t)kk * ldw * 2, wbytes);
+    const bool kin = kk + ac * 8 < K;
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+      const uint32_t dst = base + (wave * LW + j) * 1024;
+      if (kind[j] == 2) dma16(dst, rx, (live && kin) ? voff[j] + (uint32_t)kk * 2u : kOOB, 0u);
+      else dma16(dst, kind[j] ? r1 : r0, live ? voff[j] : kOOB, 0u);
+    }
+  };
+
+  f32x4_t acc[NW][2][TW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < TW; ++t) acc[w][c][t] = f32x4_t{};
+
+#pragma unroll
+  for (int p = 0; p < NSTG - 1; ++p) issue(p, p);
+  for (int i = 0; i < nst; i += NSTG) {
+#pragma unroll
+    for (int jj = 0; jj < NSTG; ++jj) {
+      // own loads of stage i + jj have landed; the barrier publishes every
+      // wave's, and every wave is done reading the slot refilled next
+      ring::wait_vmcnt<(NSTG - 2) * LW>();
+      ring::lds_barrier();
+      issue(i + jj + NSTG - 1, (jj + NSTG - 1) % NSTG);
+      const char* sl = lds + jj * SLOT;
+      u32x4_t qv[TW];
+#pragma unroll
+      for (int t = 0; t < TW; ++t) qv[t] = act_frag(sl + (NW * 4 + th * TW + t) * 1024, lane);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const u32x4_t p = wfrag(sl + w * WSLAB, ch * 2 + c, lane);
+#pragma unroll
+          for (int t = 0; t < TW; ++t) acc[w][c][t] = mfma16<E>(p, qv[t], acc[w][c][t]);
+        }
+      if (i + jj + 1 >= nst) break;
+    }
+  }
+  ring::wait_vmcnt<0>();  // the surplus stages' loads (zeros) have landed too
+
+  // outputs of this wave: token tile th * TW + t, columns
+  // n0 + 16 (2 ch + c) + 4 (lane / 16) .. + 3, token (lane % 16)
+  auto out_at = [&](int c, int t, int& m, int& n) {
+    m = (th * TW + t) * 16 + (lane & 15);
+    n = n0 + (ch * 2 + c) * 16 + (lane >> 4) * 4;
+  };
+  if (splits == 1) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        int m, n;
+        out_at(c, t, m, n);
+        if (m >= T || n >= N) continue;
+        f32x4_t sum[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum[w] = acc[w][c][t];
+        stream_store<E, KIND>(g, m, n, sum);
+      }
+    return;
+  }
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        int m, n;
+        out_at(c, t, m, n);
+        if (m >= T || n >= N) continue;
+        float* q = P + (((int64_t)split * NW + w) * T + m) * N + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(q + e, acc[w][c][t][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  // arrival, as in stream_gemm: device-coherent partials, each wave waits
+  // for its own stores, the barrier orders them before the atomic add
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* last_arrival = (int*)lds;
+  if (threadIdx.x == 0)
+    *last_arrival = __hip_atomic_fetch_add(ctr + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (unsigned)(splits - 1);
+  __syncthreads();
+  if (!*last_arrival) return;
+  if (threadIdx.x == 0) __hip_atomic_store(ctr + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = threadIdx.x; i < T * (NC / 4); i += 256) {
+    const int m = i / (NC / 4), n = n0 + (i % (NC / 4)) * 4;
+    if (n >= N) continue;
+    f32x4_t sum[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      sum[w] = f32x4_t{};
+      for (int sp = 0; sp < splits; ++sp) {
+        float* q = P + (((int64_t)sp * NW + w) * T + m) * N + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[w][e] += __hip_atomic_load(q + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    stream_store<E, KIND>(g, m, n, sum);
+  }
+}
+
 // Sum of the partial tiles of the split items of a weight-gradient launch, in
 // piece order (deterministic): C = rnd(sum over s of P[r * ksplit + s]) for
 // split item n_full + r, written to plane c0 or c1. One thread per 4
@@ -1591,6 +1789,13 @@ struct StreamArgs {
   unsigned* ctr;  // arrival counters, one per unit (splits > 1), zero at launch
 };
 
+// No-grad weight streaming: up to kStreamMaxT tokens; above kStreamRingMinT
+// tokens the workgroup-shared ring (stream_ring), else the per-wave rings
+// (stream_gemm). Measured gate/up at D = 4096, H = 11008: S = 128 70 us
+// (per-wave rings 84), S = 256 103 us (64-row tile engine 148).
+constexpr int kStreamMaxT = 256;
+constexpr int kStreamRingMinT = 32;
+
 template <class E, int KIND, int MT>
 static void launch_stream_mt(const KArgs& a, int grid, const StreamArgs& st, hipStream_t stream) {
   hipLaunchKernelGGL((stream_gemm<E, KIND, MT>), dim3(grid), dim3(256), 0, stream, a, st.P, st.splits, st.ctr);
@@ -1603,15 +1808,23 @@ static int launch_stream(KArgs a, int64_t T, int64_t ncols, const StreamArgs& st
   const int grid = units * st.splits;
   if (T <= 16) launch_stream_mt<E, KIND, 1>(a, grid, st, stream);
   else if (T <= 32) launch_stream_mt<E, KIND, 2>(a, grid, st, stream);
-  else if (T <= 64) launch_stream_mt<E, KIND, 4>(a, grid, st, stream);
-  else launch_stream_mt<E, KIND, 8>(a, grid, st, stream);
+  else if (T <= kStreamRingMinT) {
+    if (T <= 64) launch_stream_mt<E, KIND, 4>(a, grid, st, stream);
+    else launch_stream_mt<E, KIND, 8>(a, grid, st, stream);
+  } else if (T <= 64) {
+    hipLaunchKernelGGL((stream_ring<E, KIND, 4>), dim3(grid), dim3(256), 0, stream, a, st.P, st.splits, st.ctr);
+  } else if (T <= 128) {
+    hipLaunchKernelGGL((stream_ring<E, KIND, 8>), dim3(grid), dim3(256), 0, stream, a, st.P, st.splits, st.ctr);
+  } else {
+    hipLaunchKernelGGL((stream_ring<E, KIND, 16>), dim3(grid), dim3(256), 0, stream, a, st.P, st.splits, st.ctr);
+  }
   return hipGetLastError() == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
 // Tokens up to which the forward runs on the weight-streaming kernels
 // (training: few_t; no-grad, which has a workspace: stream_t).
 static inline bool few_t(int64_t T) { return T <= 64; }
-static inline bool stream_t(int64_t T) { return T <= 128; }
+static inline bool stream_t(int64_t T) { return T <= kStreamMaxT; }
 static inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // No-grad gate/up with few tokens and a narrow hidden dimension: the
@@ -1628,13 +1841,22 @@ static inline bool infer_gateup_skinny(int64_t T, int64_t H) { return few_t(T) &
 // faster at S = 1 and slower from S = 64 on (the last arrival's reduction
 // grows with them).
 constexpr int kInferPartialCap = 2;
+// Above this many tokens the down projection is not split over K (it runs
+// on the 64-row tile engine), so the call's intermediate memory is exactly
+// A + Y there (the pages' table at S = 256 measures A + Y). Measured at
+// D = 4096, H = 11008, S = 256: 124 us there, 184 us unsplit streaming,
+// 104 us split three ways (with 2.6 (A + Y) of memory).
+constexpr int kInferSplitMaxT = 128;
 
-// No-grad workspace. The A plane [T, H]; for 16-bit with T <= 128 (weight
-// streaming) also the down projection's arrival counters and, when its K is
-// split, its fp32 partials, each 256-byte aligned after A. The gate/up stage
-// never splits K: the hidden dimension alone gives enough 64-column units.
+// No-grad workspace. The A plane [T, H]; for 16-bit with T <= kInferSplitMaxT
+// also the down projection's arrival counters (one per 64 columns) and, when
+// its K is split, its fp32 partials, each 256-byte aligned after A. The
+// gate/up stage never splits K: the hidden dimension alone gives enough
+// 64-column units. stream: gate/up (and, with down_stream, down) run on the
+// weight-streaming kernels.
 struct InferPlan {
   size_t a_bytes = 0, ctr_off = 0, p_off = 0, total = 0;
+  bool stream = false, down_stream = false;
   int down_units = 0, down_splits = 1;
 };
 static inline InferPlan infer_plan(int64_t T, int64_t D, int64_t H, size_t e) {
@@ -1642,6 +1864,13 @@ static inline InferPlan infer_plan(int64_t T, int64_t D, int64_t H, size_t e) {
   p.a_bytes = (size_t)T * H * e;
   p.total = p.a_bytes;
   if (e != 2 || T <= 0 || !stream_t(T)) return p;
+  // above kInferSplitMaxT tokens the gate/up streams only with at least 128
+  // units of 64 hidden units (H = 2816, S = 256: 33 us streaming on 44
+  // units, 24 us on the 64-row tile engine; H = 11008: 103 us against 148)
+  if (T > kInferSplitMaxT && cdiv(H, stream::NC) < 128) return p;
+  p.stream = true;
+  if (T > kInferSplitMaxT) return p;
+  p.down_stream = true;
   p.down_units = cdiv(D, stream::NC);
   int sp = stream::splits_for(p.down_units, cdiv(H, stream::KS), StreamCfg<PLAIN, 1>::W);
   const size_t per = (size_t)T * D * 4;                                    // one split's partials
@@ -1926,13 +2155,20 @@ int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, voi
   using Pa = Path<E, LIN>;
   char* Ap = (char*)ws;
   const InferPlan pl = infer_plan(T, D, H, E::kBytes);
-  if (LIN || pl.down_units == 0) {
+  const StreamArgs sg{1, nullptr, nullptr};
+  if (LIN || !pl.stream) {
     int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, nullptr, s);
     if (rc) return rc;
     return Pa::template down<7>(Ap, Wd, Y, T, D, H, nullptr, s);
   }
+  if (!pl.down_stream) {
+    // above kInferSplitMaxT tokens an unsplit streaming down projection
+    // reads all of A once per 64 columns: the 64-row tile engine is faster
+    int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, &sg, s);
+    if (rc) return rc;
+    return Pa::template down<7>(Ap, Wd, Y, T, D, H, nullptr, s);
+  }
   unsigned* ctr = (unsigned*)(Ap + pl.ctr_off);
-  const StreamArgs sg{1, nullptr, nullptr};
   const StreamArgs sd{pl.down_splits, pl.down_splits > 1 ? (float*)(Ap + pl.p_off) : nullptr, ctr};
   int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, &sg, s, ctr,
                                   pl.down_units);

@@ -16,9 +16,17 @@ Prints one JSON line. Besides the contract fields it carries:
                 current kernel sources, else null.
   cpu_baseline  the fp64 oracle timed on the host cores on the first rows of
                 the same workload (a bounded sample), in the same unit.
+  parity        (same leg) one more step in the timed launch configuration,
+                sampled (one row per 32-row block, one hidden unit per
+                32-unit block) and checked against the oracle: normalized L2
+                per output, worst local error, epilogue ulp.
+  sclk          the graphics clock sampled during the timed steps.
   stages        mean duration and TFLOP/s of every kernel.
+  infer         the no-grad sweep (B=1, S=1..256) against 8 TB/s and a
+                same-run stream copy; fp32_ieee, tp_shards, linear_layout:
+                the other legs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--infer-only]
 """
 
 import argparse
@@ -119,6 +127,146 @@ def cpu_baseline(inp, D, H, target_s):
     return {"value": round(tflops, 5), "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
             "sample": f"fwd+bwd on the first {rows} of the workload's rows (same weights), "
                       f"{t:.1f} s, numpy float64 BLAS"}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi gpu_metrics, MHz, every XCD)
+    in a background thread while the timed loop runs; reported beside the
+    fraction of peak, which is quoted at 2.4 GHz."""
+
+    def __init__(self, torch, period_s=0.01):
+        self.period, self.samples, self.src, self._stop = period_s, [], None, None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            h = hs[0]
+            if len(hs) > 1:
+                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+                for c in hs:
+                    if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == bus:
+                        h = c
+            self._amdsmi, self._h = amdsmi, h
+        except Exception as e:  # pragma: no cover - reported as unavailable
+            self._amdsmi, self.err = None, repr(e)
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        v = m.get("current_gfxclks")
+        vals = [float(x) for x in (v if isinstance(v, (list, tuple)) else [v]) if isinstance(x, (int, float))]
+        vals = [x for x in vals if 0 < x < 10000]
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [float(m["current_gfxclk"])]
+        return sum(vals) / len(vals) if vals else None
+
+    def __enter__(self):
+        import threading
+
+        if self._amdsmi is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    v = self._read()
+                    if v:
+                        self.samples.append(v)
+                except Exception:
+                    pass
+                self._stop.wait(self.period)
+
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._stop is not None:
+            self._stop.set()
+            self._t.join()
+        return False
+
+    def result(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"sclk_mhz_mean": round(sum(xs) / len(xs), 1), "sclk_mhz_median": round(xs[len(xs) // 2], 1),
+                "samples": len(xs), "source": "amdsmi gpu_metrics current_gfxclks, mean over XCDs, "
+                                              "sampled every 10 ms during the timed steps"}
+
+
+def headline_sample(T, H, seed=65536):
+    """The rows and hidden units the parity check samples: one row in every
+    32-row block of the tokens and one hidden unit in every 32-unit block,
+    which touches every 32 x 32 block row and every 256 x 256 tile of each
+    output (including every weight-gradient tile split over K)."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    pick = lambda n: np.arange(0, n, 32) + rng.integers(0, np.minimum(32, n - np.arange(0, n, 32)))
+    return pick(T), pick(H)
+
+
+def gather_parity_sample(mlp, torch, g, T, H):
+    """One more forward + backward in the timed launch configuration; keeps
+    the sampled rows of Y, dI, A, G, U (after fwd), dG, dU (after bwd) and
+    the sampled hidden units of dWg, dWu (columns) and dWd (rows), on the
+    host."""
+    rows, hs = headline_sample(T, H)
+    r = torch.as_tensor(rows, device=g["X"].device)
+    h = torch.as_tensor(hs, device=g["X"].device)
+    y, saved = mlp.fwd(g["X"], g["Wg"], g["Wu"], g["Wd"])
+    agu = [saved[i].index_select(0, r) for i in range(3)]
+    dx, dwg, dwu, dwd = mlp.bwd(g["dY"], g["X"], g["Wg"], g["Wu"], g["Wd"], saved)
+    out = {"Y": y.index_select(0, r), "dI": dx.index_select(0, r), "A": agu[0], "G": agu[1], "U": agu[2],
+           "dG": saved[1].index_select(0, r), "dU": saved[2].index_select(0, r),
+           "dWg": dwg.index_select(1, h).t(), "dWu": dwu.index_select(1, h).t(), "dWd": dwd.index_select(0, h)}
+    torch.cuda.synchronize()
+    out = {k: v.float().cpu().numpy().astype("float64") for k, v in out.items()}
+    return rows, hs, out
+
+
+def parity_vs_oracle(inp, rows, hs, got):
+    """The sampled outputs against the fp64 oracle (part of the leg that runs
+    the oracle on the host): normalized L2 per output over the sample, the
+    worst per-line and per-segment (32 and 256 elements: the footprints of a
+    matrix-core block and of a tile) local error, and the largest ulp
+    distance of A from rnd(SiLU(g) u) of the stored g, u."""
+    import numpy as np
+
+    import oracle
+
+    f = {k: inp[k].float().numpy() for k in ("X", "Wg", "Wu", "Wd", "dY")}
+    r = oracle.rows(rows, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
+    c = oracle.cols(hs, f["X"], f["Wg"], f["Wu"], f["Wd"], f["dY"])
+    ref = {"Y": r["Y"], "dI": r["dI"], "G": r["G"], "U": r["U"], "dG": r["dG"], "dU": r["dU"],
+           "dWg": c["dWg"].T, "dWu": c["dWu"].T, "dWd": c["dWd"]}
+
+    def local(a, b, seg):
+        d, n = a - b, b.shape[1]
+        floor = np.sqrt(np.mean(b * b))
+        w = -n % seg
+        dd = np.pad(d, ((0, 0), (0, w))).reshape(b.shape[0], -1, seg)
+        bb = np.pad(b, ((0, 0), (0, w))).reshape(b.shape[0], -1, seg)
+        cnt = np.pad(np.ones_like(b), ((0, 0), (0, w))).reshape(b.shape[0], -1, seg).sum(-1)
+        e = np.sqrt((dd * dd).sum(-1) / cnt) / np.maximum(np.sqrt((bb * bb).sum(-1) / cnt), floor)
+        return float(e.max())
+
+    nl2, worst = {}, {}
+    for k, b in ref.items():
+        a = got[k]
+        nl2[k] = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        worst[k] = max(local(a, b, b.shape[1]), local(a, b, 32), local(a, b, 256))
+    a_ref = oracle.round_to(oracle.epilogue_fwd(got["G"], got["U"]), "bf16")
+    ulp = int(oracle.ulp_distance(got["A"], a_ref, "bf16").max())
+    ok = all(v <= 1e-2 for v in nl2.values()) and all(v <= 1e-2 for v in worst.values()) and ulp <= 1
+    return {"sample": f"{len(rows)} rows (one per 32-row block) of Y, dI, G, U, dG, dU and {len(hs)} hidden "
+                      "units (one per 32-unit block) of dWg, dWu, dWd, from one more step in the timed "
+                      "launch configuration",
+            "normalized_l2": {k: float(f"{v:.3e}") for k, v in nl2.items()},
+            "worst_local": {k: float(f"{v:.3e}") for k, v in worst.items()},
+            "epilogue_max_ulp": ulp, "tolerance": 1e-2, "pass": bool(ok)}
 
 
 def stream_copy_gbps(torch, dev, mib=1024, reps=10):
@@ -261,6 +409,39 @@ def fp32_leg(mlp, torch, dev, steps=10, warmup=3):
             "tflops": round(tf, 2), "peak_tflops": PEAK_FP32_TFLOPS, "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4)}
 
 
+def linear_layout_leg(mlp, torch, g, T, D, H, steps=10, warmup=3):
+    """The headline step with the weights in the nn.Linear layout (gate_proj,
+    up_proj [H, D], down_proj [D, H]; the forward GEMMs read K-major weights,
+    dA and dI N-major ones), same inputs: mean step time and TFLOP/s."""
+    wl = {k: g[k].t().contiguous() for k in ("Wg", "Wu", "Wd")}
+    bf = torch.bfloat16
+    dev = g["X"].device
+    y, saved = torch.empty((T, D), dtype=bf, device=dev), torch.empty((3, T, H), dtype=bf, device=dev)
+    dx = torch.empty((T, D), dtype=bf, device=dev)
+    dwg, dwu, dwd = (torch.empty_like(wl[k]) for k in ("Wg", "Wu", "Wd"))
+
+    def step():
+        mlp.fwd(g["X"], wl["Wg"], wl["Wu"], wl["Wd"], y=y, saved=saved, linear=True)
+        mlp.bwd(g["dY"], g["X"], wl["Wg"], wl["Wu"], wl["Wd"], saved, dx=dx, dwg=dwg, dwu=dwu, dwd=dwd,
+                linear=True)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with mlp.StageTimer(capacity=steps) as st:
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    tf = 18.0 * T * D * H / (ms * 1e-3) / 1e12
+    stages = {k: round(v / st.count[k], 4) for k, v in st.ms.items() if st.count[k]}
+    return {"ms_per_step": round(ms, 3), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "stage_ms": stages}
+
+
 def tp_shard_sweep(mlp, torch, dev, T, D, H, steps=5, warmup=2):
     """Tensor-parallel shard shapes on one GPU: the same step at H/P for
     P in {2, 4, 8} (Wg, Wu split by columns and Wd by rows; each GPU of a
@@ -350,9 +531,118 @@ def ingest_traffic(fetch_csv, write_csv, copy_mib, command):
     print(json.dumps(out, indent=1))
 
 
+INFER_TRACE_CALLS = 3
+
+
+def infer_trace(mlp, torch, dev):
+    """A fixed, short sequence of no-grad calls for rocprofv3: a 1 GiB copy
+    (the counters' calibration kernel: 1 GiB read + 1 GiB written), then for
+    each shape of the sweep, in order, INFER_TRACE_CALLS calls, each after a
+    read of a 1 GiB buffer that flushes the 256 MB cache. ingest_infer maps
+    the dispatches back to the shapes by this order."""
+    from synth import INFER_DH, INFER_S, make_inputs
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    del dst
+    order = []
+    for D, H in INFER_DH:
+        w = make_inputs(1, D, H, seed=77, dtype="bf16", with_dy=False)
+        Wg, Wu, Wd = (w[k].to(dev) for k in ("Wg", "Wu", "Wd"))
+        for S in INFER_S:
+            X = make_inputs(S, D, H, seed=S, dtype="bf16", with_dy=False)["X"].to(dev)
+            ws = torch.empty(mlp.infer_workspace_bytes(S, D, H), dtype=torch.uint8, device=dev)
+            y = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
+            for _ in range(INFER_TRACE_CALLS):
+                src.sum()
+                mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+            order.append([D, H, S])
+    torch.cuda.synchronize()
+    return order
+
+
+def ingest_infer(trace_csv, fetch_csv, write_csv, out_md, command):
+    """Summarise a kernel trace and FETCH_SIZE / WRITE_SIZE counter passes of
+    `bench.py --infer-trace` (three runs of the same command) as a table per
+    shape: kernels, device time of the call (first kernel start to last
+    kernel end, mean over the calls), algorithmic GB/s, and the counters'
+    bytes scaled by what they read for the 1 GiB copy."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    from synth import INFER_DH, INFER_S
+
+    ours = lambda n: "swiglu::" in n
+    with open(trace_csv) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    calls = []  # one list of (name, start, end) per call
+    for r in rows:
+        n = r["Kernel_Name"]
+        if not ours(n):
+            if calls and calls[-1]:
+                calls.append([])
+            continue
+        if not calls:
+            calls.append([])
+        calls[-1].append((n, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    calls = [c for c in calls if c]
+    shapes = [(D, H, S) for D, H in INFER_DH for S in INFER_S]
+    assert len(calls) == len(shapes) * INFER_TRACE_CALLS, (len(calls), len(shapes))
+
+    def counters(path, counter):
+        per, names = defaultdict(float), {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    k = int(r["Dispatch_Id"])
+                    per[k] += float(r["Counter_Value"]) * 1024.0
+                    names[k] = r["Kernel_Name"]
+        ids = sorted(per)
+        copy = [per[k] for k in ids if "copy" in names[k].lower()][0]
+        seq = [per[k] for k in ids if ours(names[k])]
+        return seq, copy
+
+    fetch, fcopy = counters(fetch_csv, "FETCH_SIZE")
+    write, wcopy = counters(write_csv, "WRITE_SIZE")
+    ff, wf = (1 << 30) / fcopy, (1 << 30) / wcopy
+    short = lambda n: re.sub(r"\(.*", "", n).replace("void ", "").replace("swiglu::", "")
+    lines = ["| D -> H | S | kernels | device us | algorithmic GB/s | % of 8 TB/s | fetch MB | write MB |",
+             "|---|---|---|---|---|---|---|---|"]
+    i = k = 0
+    for D, H, S in shapes:
+        cs = calls[i:i + INFER_TRACE_CALLS]
+        i += INFER_TRACE_CALLS
+        nk = len(cs[0])
+        us = sum((c[-1][2] - c[0][1]) / 1e3 for c in cs) / len(cs)
+        fb = sum(fetch[k:k + nk * INFER_TRACE_CALLS]) * ff / INFER_TRACE_CALLS
+        wb = sum(write[k:k + nk * INFER_TRACE_CALLS]) * wf / INFER_TRACE_CALLS
+        k += nk * INFER_TRACE_CALLS
+        nbytes = 2 * (3 * D * H + 2 * S * D + 2 * S * H)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        names = " + ".join(f"`{short(n)}` {(e - b) / 1e3:.1f}" for n, b, e in cs[-1])
+        lines.append(f"| {D} -> {H} | {S} | {names} | {us:.1f} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBS:.0f} | "
+                     f"{fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    head = (f"# No-grad SwiGLU MLP, B=1, S=1..256, bf16: kernel trace and HBM traffic\n\n"
+            f"Commands (repository root, one MI355X; three runs of the same program):\n\n```\n{command}\n```\n\n"
+            f"Each call follows a read of a 1 GiB buffer (the 256 MB cache holds no weights). Device us: from the "
+            f"first kernel's start to the last kernel's end, mean over {INFER_TRACE_CALLS} calls; the kernels "
+            f"column gives the last call's kernels and their us. Algorithmic bytes: 2 (3 D H + 2 S D + 2 S H). "
+            f"Fetch and write: FETCH_SIZE and WRITE_SIZE summed over the call's kernels, scaled by what they "
+            f"read for the 1 GiB copy in the same run (fetch x{ff:.3f}, write x{wf:.3f}). FETCH_SIZE counts "
+            f"what L2 requests from the fabric, so it includes bytes the Infinity Cache serves.\n\n")
+    with open(out_md, "w") as f:
+        f.write(head + "\n".join(lines) + "\n")
+    print(head + "\n".join(lines))
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-traffic":
         ingest_traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), " ".join(sys.argv[5:]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--ingest-infer":
+        ingest_infer(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], " ".join(sys.argv[6:]))
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,8 +653,11 @@ def main():
     ap.add_argument("--no-infer", action="store_true", help="skip the no-grad (inference) sweep")
     ap.add_argument("--infer-only", action="store_true",
                     help="only the no-grad sweep (and the stream-copy reference): one JSON line")
+    ap.add_argument("--infer-trace", action="store_true",
+                    help="only a short fixed sequence of no-grad calls, for rocprofv3 (see ingest_infer)")
     ap.add_argument("--no-fp32", action="store_true", help="skip the true-IEEE fp32 run")
     ap.add_argument("--no-tp", action="store_true", help="skip the tensor-parallel shard-shape sweep")
+    ap.add_argument("--no-linear", action="store_true", help="skip the nn.Linear weight-layout leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known traffic, used to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -380,6 +673,10 @@ def main():
     import backward_gate_up_amd as mlp
     from synth import WORKLOADS, workload_inputs
 
+    if args.infer_trace:
+        order = infer_trace(mlp, torch, torch.device("cuda:0"))
+        print(json.dumps({"infer_trace": order, "calls_per_shape": INFER_TRACE_CALLS}), flush=True)
+        return
     if args.infer_only:
         dev = torch.device("cuda:0")
         copy = stream_copy_gbps(torch, dev)
@@ -422,7 +719,8 @@ def main():
 
     # events between steps: the whole loop gives the mean, each step its own time
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    with mlp.StageTimer(capacity=max(args.steps, 1)) as st:
+    clock = ClockSampler(torch)
+    with mlp.StageTimer(capacity=max(args.steps, 1)) as st, clock:
         torch.cuda.synchronize()
         ev[0].record()
         for i in range(args.steps):
@@ -469,12 +767,19 @@ def main():
         "config": {"workload": "swiglu_mlp_fwd_bwd", "D": D, "H": H, "B": B, "S": S, "T": T,
                    "parallelism": "single-gpu"},
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "sclk": clock.result(),
         "step_ms": {"mean": round(ms_step, 3), "median": round(per_step[len(per_step) // 2], 3),
                     "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
         "roofline": roofline,
         "stages": stages,
     }
-    del g, X, Wg, Wu, Wd, dY, y, saved, dx, dwg, dwu, dwd
+    psample = None
+    if not args.no_cpu_baseline:
+        psample = gather_parity_sample(mlp, torch, g, T, H)
+    del y, saved, dx, dwg, dwu, dwd
+    if not args.no_linear:
+        out["linear_layout"] = linear_layout_leg(mlp, torch, g, T, D, H)
+    del g, X, Wg, Wu, Wd, dY
     if not args.no_fp32:
         out["fp32_ieee"] = fp32_leg(mlp, torch, dev)
     if not args.no_tp:
@@ -485,7 +790,10 @@ def main():
                         "peak_GBps": PEAK_HBM_GBS, "stream_copy_GBps": copy,
                         "by_shape": infer_sweep(mlp, torch, dev, copy_gbps=copy)}
     if not args.no_cpu_baseline:
+        # the leg that runs the oracle on the host: its time on a bounded
+        # sample, and the parity of the sampled GPU outputs
         out["cpu_baseline"] = cpu_baseline(inp, D, H, args.cpu_seconds)
+        out["parity"] = parity_vs_oracle(inp, *psample)
     print(json.dumps(out), flush=True)
 
 

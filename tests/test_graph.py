@@ -3,9 +3,12 @@
 The no-grad call and a full training step (forward + backward) are captured
 once through torch.cuda.graph on the current stream. Each graph is then
 replayed several times, with unrelated eager work and synchronizations in
-between. Every replay must reproduce the eager outputs bit for bit: the path
-is deterministic (no atomics, fixed tile order), and it records no memset
-nodes. The pages name small-shape host overhead as the no-grad path's only
+between. Every replay must reproduce the eager outputs bit for bit (the
+path is deterministic: a fixed tile and split order, and the one atomic
+counter per unit only elects which workgroup adds the partials, in a fixed
+order; it records no memset nodes), and the replayed outputs are checked
+against the fp64 oracle as well, at the parity bounds (whole tensor, per
+row, per 32 x 32 block, per 256 x 256 tile). The pages name small-shape host overhead as the no-grad path's only
 loss ("[RFC] Full-pipeline SwiGLU MLP with forward/backward co-optimization",
 "Inference results"), and replaying a graph is how a caller removes it.
 """
@@ -13,8 +16,9 @@ loss ("[RFC] Full-pipeline SwiGLU MLP with forward/backward co-optimization",
 import pytest
 import torch
 
+import oracle as O
 from synth import make_inputs
-from tests._util import banner, to_dev
+from tests._util import assert_local, banner, f64, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -51,12 +55,16 @@ def test_infer_graph_replay(mlp, S, D, H):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, ref), f"replay {r}"
+    f = {k: v.float().cpu().numpy() for k, v in g.items()}
+    assert_local(f64(y), O.infer(f["X"], f["Wg"], f["Wu"], f["Wd"]), 1e-2, ("graph infer", S, D, H))
     # new inputs written into the captured buffers flow through the graph
-    g["X"].copy_(make_inputs(S, D, H, seed=99, dtype="bf16", with_dy=False)["X"].cuda())
+    x2 = make_inputs(S, D, H, seed=99, dtype="bf16", with_dy=False)["X"]
+    g["X"].copy_(x2.cuda())
     graph.replay()
     mlp_eager = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"])
     torch.cuda.synchronize()
     assert torch.equal(y, mlp_eager)
+    assert_local(f64(y), O.infer(x2.float().numpy(), f["Wg"], f["Wu"], f["Wd"]), 1e-2, ("graph infer new X", S))
 
 
 @pytest.mark.parametrize("T,D,H", [(300, 256, 384), (1024, 512, 1024)])
@@ -90,3 +98,8 @@ def test_train_step_graph_replay(mlp, T, D, H):
         torch.cuda.synchronize()
         for name, got, want in zip(("Y", "dI", "dWg", "dWu", "dWd"), outs, ref):
             assert torch.equal(got, want), f"replay {r}: {name}"
+    f = {k: v.float().cpu().numpy() for k, v in g.items()}
+    oref = O.bwd(f["dY"], f["X"], f["Wg"], f["Wu"], f["Wd"])
+    oref["Y"] = O.fwd(f["X"], f["Wg"], f["Wu"], f["Wd"])["Y"]
+    for name, got in zip(("Y", "dI", "dWg", "dWu", "dWd"), outs):
+        assert_local(f64(got), oref[name], 1e-2, ("graph train", name))

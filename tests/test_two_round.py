@@ -85,14 +85,15 @@ def test_two_round_epilogue(mlp, fmt, dt, T, D, H):
     if fmt == "bf16" and T * H >= 100000:
         assert 0.2 < diff < 0.35
     assert diff > 0.0
-    # no-grad path: above 128 tokens the same kernels, so the same Y; up to
-    # 128 tokens it runs the split-K kernels (another summation order), which
-    # must agree within the bound and differ from their own one-round result
+    # no-grad path: above 256 tokens the same kernels, so the same Y; up to
+    # 256 tokens it runs the weight-streaming kernels (another summation
+    # order), which must agree within the bound and differ from their own
+    # one-round result
     ws = torch.empty(mlp.infer_workspace_bytes(T, D, H, dt), dtype=torch.uint8, device="cuda")
     y_ng = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], workspace=ws, two_round=True)
     y_ng1 = mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"], workspace=ws, two_round=False)
     torch.cuda.synchronize()
-    if T > 128:
+    if T > 256:
         assert torch.equal(y_ng, y2)
     else:
         assert nl2(f64(y_ng), f64(y2)) <= TOL[fmt]
