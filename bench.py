@@ -20,7 +20,8 @@ Prints one JSON line. Besides the contract fields it carries:
                 sampled (one row per 32-row block, one hidden unit per
                 32-unit block) and checked against the oracle: normalized L2
                 per output, worst local error, epilogue ulp.
-  sclk          the graphics clock sampled during the timed steps.
+  sclk          the graphics clock (amdsmi) while the step repeats for 3 s
+                after the timed steps.
   stages        mean duration and TFLOP/s of every kernel.
   infer         the no-grad sweep (B=1, S=1..256) against 8 TB/s and a
                 same-run stream copy; fp32_ieee, tp_shards, linear_layout:
@@ -129,71 +130,58 @@ def cpu_baseline(inp, D, H, target_s):
                       f"{t:.1f} s, numpy float64 BLAS"}
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi gpu_metrics, MHz, every XCD)
-    in a background thread while the timed loop runs; reported beside the
-    fraction of peak, which is quoted at 2.4 GHz."""
+def measure_clock(torch, step, seconds=3.0, settle=1.5, period=0.05):
+    """The graphics clock while the step runs: amdsmi's gpu_metrics
+    (current_gfxclks, one value per XCD, in MHz) sampled every `period` s
+    while the step repeats for `seconds`, outside the timed region. The
+    metrics are refreshed about once a second, so samples from the first
+    `settle` seconds (which can still show the idle clock) are dropped.
+    Reported beside the fraction of peak, which is quoted at 2.4 GHz."""
+    import threading
 
-    def __init__(self, torch, period_s=0.01):
-        self.period, self.samples, self.src, self._stop = period_s, [], None, None
-        try:
-            import amdsmi
+    try:
+        import amdsmi
 
-            amdsmi.amdsmi_init()
-            hs = amdsmi.amdsmi_get_processor_handles()
-            h = hs[0]
-            if len(hs) > 1:
-                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
-                for c in hs:
-                    if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == bus:
-                        h = c
-            self._amdsmi, self._h = amdsmi, h
-        except Exception as e:  # pragma: no cover - reported as unavailable
-            self._amdsmi, self.err = None, repr(e)
+        amdsmi.amdsmi_init()
+        hs = amdsmi.amdsmi_get_processor_handles()
+        h = hs[0]
+        if len(hs) > 1:
+            bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            for c in hs:
+                if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == bus:
+                    h = c
+    except Exception as e:  # pragma: no cover - reported as unavailable
+        return {"error": repr(e)}
+    samples, stop = [], threading.Event()
+    t0 = time.perf_counter()
 
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
-        v = m.get("current_gfxclks")
-        vals = [float(x) for x in (v if isinstance(v, (list, tuple)) else [v]) if isinstance(x, (int, float))]
-        vals = [x for x in vals if 0 < x < 10000]
-        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
-            vals = [float(m["current_gfxclk"])]
-        return sum(vals) / len(vals) if vals else None
+    def sample():
+        while not stop.is_set():
+            try:
+                v = amdsmi.amdsmi_get_gpu_metrics_info(h).get("current_gfxclks")
+                xs = [float(x) for x in (v if isinstance(v, (list, tuple)) else [v]) if isinstance(x, (int, float))]
+                xs = [x for x in xs if 0 < x < 10000]
+                if xs and time.perf_counter() - t0 >= settle:
+                    samples.append(sum(xs) / len(xs))
+            except Exception:
+                pass
+            stop.wait(period)
 
-    def __enter__(self):
-        import threading
-
-        if self._amdsmi is None:
-            return self
-        self._stop = threading.Event()
-
-        def run():
-            while not self._stop.is_set():
-                try:
-                    v = self._read()
-                    if v:
-                        self.samples.append(v)
-                except Exception:
-                    pass
-                self._stop.wait(self.period)
-
-        self._t = threading.Thread(target=run, daemon=True)
-        self._t.start()
-        return self
-
-    def __exit__(self, *exc):
-        if self._stop is not None:
-            self._stop.set()
-            self._t.join()
-        return False
-
-    def result(self):
-        if not self.samples:
-            return None
-        xs = sorted(self.samples)
-        return {"sclk_mhz_mean": round(sum(xs) / len(xs), 1), "sclk_mhz_median": round(xs[len(xs) // 2], 1),
-                "samples": len(xs), "source": "amdsmi gpu_metrics current_gfxclks, mean over XCDs, "
-                                              "sampled every 10 ms during the timed steps"}
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    xs = sorted(samples)
+    return {"sclk_mhz_mean": round(sum(xs) / len(xs), 1), "sclk_mhz_min": round(xs[0], 1),
+            "sclk_mhz_max": round(xs[-1], 1), "samples": len(xs),
+            "source": f"amdsmi gpu_metrics current_gfxclks (mean over XCDs; refreshed about once a second), "
+                      f"sampled every {period} s while the step repeated for {seconds} s after the timed "
+                      f"steps; the first {settle} s dropped"}
 
 
 def headline_sample(T, H, seed=65536):
@@ -719,8 +707,7 @@ def main():
 
     # events between steps: the whole loop gives the mean, each step its own time
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    clock = ClockSampler(torch)
-    with mlp.StageTimer(capacity=max(args.steps, 1)) as st, clock:
+    with mlp.StageTimer(capacity=max(args.steps, 1)) as st:
         torch.cuda.synchronize()
         ev[0].record()
         for i in range(args.steps):
@@ -767,7 +754,7 @@ def main():
         "config": {"workload": "swiglu_mlp_fwd_bwd", "D": D, "H": H, "B": B, "S": S, "T": T,
                    "parallelism": "single-gpu"},
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "sclk": clock.result(),
+        "sclk": measure_clock(torch, step),
         "step_ms": {"mean": round(ms_step, 3), "median": round(per_step[len(per_step) // 2], 3),
                     "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
         "roofline": roofline,
