@@ -519,6 +519,161 @@ def ingest_traffic(fetch_csv, write_csv, copy_mib, command):
     print(json.dumps(out, indent=1))
 
 
+def ingest_counters(trace_csv, pass_a_csv, pass_b_csv, out_md, command):
+    """Per-kernel clock, matrix-core occupancy, stalls and traffic of the
+    training step from a kernel trace and two counter passes of
+    `bench.py --steps 2 --warmup 1 --no-infer --no-fp32 --no-tp --no-linear
+    --no-cpu-baseline`, with profiles/traffic.json (FETCH/WRITE) when it
+    matches the sources. Means over every launch of each kernel.
+      sclk: GRBM_GUI_ACTIVE / 8 (rocprofv3 sums the 8 XCDs) / duration;
+      MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (per-XCD cycles x 1024 SIMDs);
+      effective % of peak: sclk x busy / 2.4 GHz;
+      wait: SQ_WAIT_ANY / SQ_WAVE_CYCLES (waves in s_waitcnt), LDS wait:
+      SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES, LDS conflict: SQ_LDS_BANK_CONFLICT
+      / SQ_LDS_IDX_ACTIVE, TA FIFO full: SQ_VMEM_TA_ADDR_FIFO_FULL per
+      CU-cycle."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    from backward_gate_up_amd._lib import STAGE_NAMES
+
+    def key(n):
+        m = re.search(r"(ring_gemm|ring_wgrad)<[^>]*?(\d+)>\(", n)
+        return STAGE_NAMES[int(m.group(2))] if m else None
+
+    dur = defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            k = key(r["Kernel_Name"])
+            if k:
+                dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    cnt = defaultdict(lambda: defaultdict(float))
+    disp = defaultdict(set)
+    for path in (pass_a_csv, pass_b_csv):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = key(r["Kernel_Name"])
+                if k:
+                    cnt[k][r["Counter_Name"]] += float(r["Counter_Value"])
+                    disp[(k, path)].add(r["Dispatch_Id"])
+    traffic = {}
+    tp = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tp):
+        with open(tp) as f:
+            t = json.load(f)
+        if t.get("source_sha256") == kernel_source_hash():
+            traffic = t["kernels"]
+    order = ["gateup_swiglu", "down_proj", "dgu_inplace", "dwd", "dwgu", "dx"]
+    lines = ["| kernel | ms | sclk GHz | MFMA busy % | effective % of peak | wait % | LDS wait % | "
+             "LDS conflict % | TA FIFO full % | fetch GB | write GB |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in order:
+        if k not in cnt or not dur.get(k):
+            continue
+        c = cnt[k]
+        na = len(disp[(k, pass_a_csv)]) or 1
+        nb = len(disp[(k, pass_b_csv)]) or 1
+        sel = dur[k][2:7] or dur[k]  # the timed launches of the trace run (2 warm-up, 5 timed steps)
+        ms = sum(sel) / len(sel)
+        # GRBM_GUI_ACTIVE is in both passes: per-dispatch means of each
+        cyc = c["GRBM_GUI_ACTIVE"] / (na + nb) / 8
+        sclk = cyc / (ms * 1e-3) / 1e9
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / na / (cyc * 1024)
+        wave = c["SQ_WAVE_CYCLES"] / na
+        tr = traffic.get(k, {})
+        lines.append(f"| {k} | {ms:.3f} | {sclk:.2f} | {100 * busy:.1f} | {100 * sclk * busy / 2.4:.1f} | "
+                     f"{100 * c['SQ_WAIT_ANY'] / na / wave:.1f} | {100 * c['SQ_WAIT_INST_LDS'] / na / wave:.1f} | "
+                     f"{100 * c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1f} | "
+                     f"{100 * c['SQ_VMEM_TA_ADDR_FIFO_FULL'] / nb / (cyc * 256):.1f} | "
+                     f"{tr.get('fetch_bytes_per_launch', float('nan')) / 1e9:.2f} | "
+                     f"{tr.get('write_bytes_per_launch', float('nan')) / 1e9:.2f} |")
+    head = ("# Clock, matrix-core occupancy, stalls and traffic: fused SwiGLU MLP fwd+bwd, D=4096 H=11008 "
+            "T=65536, bf16\n\nCommands (repository root, one MI355X; each pass a run of its own):\n\n```\n"
+            f"{command}\n```\n\n"
+            "Means over every launch of each kernel (the warm-up and timed steps of each run). ms: the kernel "
+            "trace (timed steps). sclk: GRBM_GUI_ACTIVE / 8 (rocprofv3 sums the 8 XCDs) over the kernel's duration. MFMA "
+            "busy: SQ_VALU_MFMA_BUSY_CYCLES / (per-XCD cycles x 1024 SIMDs). Effective % of peak: sclk x busy "
+            "/ 2.4 GHz, the clock the 2516.6 TFLOP/s peak is quoted at. Wait %: SQ_WAIT_ANY / SQ_WAVE_CYCLES "
+            "(wave-cycles in s_waitcnt, for loads or LDS). LDS wait %: SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES. LDS "
+            "conflict %: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. TA FIFO full %: SQ_VMEM_TA_ADDR_FIFO_FULL "
+            "per CU-cycle (the texture unit's address queue refusing further loads). Fetch and write: "
+            "profiles/traffic.json (FETCH_SIZE, WRITE_SIZE scaled by a 1 GiB copy in the same run), per "
+            "launch.\n\n")
+    with open(out_md, "w") as f:
+        f.write(head + "\n".join(lines) + "\n")
+    print(head + "\n".join(lines))
+
+
+def ingest_trace(trace_csv, out_md, command, warmup=2, timed=5):
+    """Per-kernel durations of the training step from a rocprofv3 kernel
+    trace (csv) of `bench.py --steps 5 --warmup 2 --no-infer
+    --no-cpu-baseline --no-fp32 --no-tp --no-linear`: the mean over the last
+    `timed` launches of each ring kernel after `warmup`, plus the split-K
+    reduction that
+    follows each weight-gradient launch, with TFLOP/s, algorithmic bytes and
+    the traffic of profiles/traffic.json when it matches the sources."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    from backward_gate_up_amd._lib import STAGE_NAMES
+
+    with open(trace_csv) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    dur, red, names = defaultdict(list), defaultdict(list), {}
+    last = None
+    for r in rows:
+        n = r["Kernel_Name"]
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+        m = re.search(r"(ring_gemm|ring_wgrad)<[^>]*?(\d+)>\(", n)
+        if m:
+            last = STAGE_NAMES[int(m.group(2))]
+            dur[last].append(d)
+            names[last] = re.sub(r"\(.*", "", n).replace("void ", "")
+        elif "splitk_reduce_tiles" in n and last:
+            red[last].append(d)
+    T, D, H = 65536, 4096, 11008
+    traffic = {}
+    tp = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tp):
+        with open(tp) as f:
+            t = json.load(f)
+        if t.get("source_sha256") == kernel_source_hash():
+            traffic = t["kernels"]
+    lines = ["| kernel | stage | trace ms | reduction ms | stage ms | TFLOP/s | % of peak | algorithmic GB | "
+             "fetch GB | write GB |", "|---|---|---|---|---|---|---|---|---|---|"]
+    total = 0.0
+    for st in ("gateup_swiglu", "down_proj", "dgu_inplace", "dwd", "dwgu", "dx"):
+        if not dur.get(st):
+            continue
+        sel = dur[st][warmup:warmup + timed]
+        ms = sum(sel) / len(sel)
+        rsel = red[st][warmup:warmup + timed] if red.get(st) else []
+        rd = sum(rsel) / len(rsel) if rsel else 0.0
+        tf = STAGE_FLOPS[st] * T * D * H / ((ms + rd) * 1e-3) / 1e12
+        total += ms + rd
+        tr = traffic.get(st, {})
+        lines.append(f"| `{names[st]}` | {st} | {ms:.3f} | {rd:.3f} | {ms + rd:.3f} | {tf:.0f} | "
+                     f"{100 * tf / PEAK_BF16_TFLOPS:.1f} | {stage_bytes(st, T, D, H, 2) / 1e9:.2f} | "
+                     f"{tr.get('fetch_bytes_per_launch', float('nan')) / 1e9:.2f} | "
+                     f"{tr.get('write_bytes_per_launch', float('nan')) / 1e9:.2f} |")
+    head = ("# Kernel trace: fused SwiGLU MLP fwd+bwd, D=4096 H=11008 T=65536 (B=8, S=8192), bf16\n\n"
+            f"Command (repository root, one MI355X):\n\n```\n{command}\n```\n\n"
+            f"Means over launches {warmup + 1} to {warmup + timed} of each kernel (the timed steps). The "
+            "weight-gradient "
+            "stages are two launches: the ring kernel, then `splitk_reduce_tiles` adding the fp32 partial "
+            "tiles of the tiles split over K. TFLOP/s from each stage's algorithmic FLOPs (4, 2, 2, 2, 4, 4 "
+            "x T D H). Algorithmic bytes: each operand read once, each result written once. Fetch / write: "
+            "profiles/traffic.json.\n\n")
+    tail = (f"\nStage times sum to {total:.2f} ms per step = {18.0 * T * D * H / (total * 1e-3) / 1e12:.0f} "
+            f"TFLOP/s ({100 * 18.0 * T * D * H / (total * 1e-3) / 1e12 / PEAK_BF16_TFLOPS:.1f} % of dense "
+            "bf16 peak).\n")
+    with open(out_md, "w") as f:
+        f.write(head + "\n".join(lines) + "\n" + tail)
+    print(head + "\n".join(lines) + "\n" + tail)
+
+
 INFER_TRACE_CALLS = 3
 
 
@@ -629,6 +784,12 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-traffic":
         ingest_traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), " ".join(sys.argv[5:]))
         return
+    if len(sys.argv) > 1 and sys.argv[1] == "--ingest-trace":
+        ingest_trace(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--ingest-counters":
+        ingest_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], " ".join(sys.argv[6:]))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-infer":
         ingest_infer(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], " ".join(sys.argv[6:]))
         return
@@ -646,6 +807,7 @@ def main():
     ap.add_argument("--no-fp32", action="store_true", help="skip the true-IEEE fp32 run")
     ap.add_argument("--no-tp", action="store_true", help="skip the tensor-parallel shard-shape sweep")
     ap.add_argument("--no-linear", action="store_true", help="skip the nn.Linear weight-layout leg")
+    ap.add_argument("--no-clock", action="store_true", help="skip the 3 s graphics-clock window (profiled runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known traffic, used to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -754,7 +916,7 @@ def main():
         "config": {"workload": "swiglu_mlp_fwd_bwd", "D": D, "H": H, "B": B, "S": S, "T": T,
                    "parallelism": "single-gpu"},
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "sclk": measure_clock(torch, step),
+        "sclk": None if args.no_clock else measure_clock(torch, step),
         "step_ms": {"mean": round(ms_step, 3), "median": round(per_step[len(per_step) // 2], 3),
                     "min": round(per_step[0], 3), "max": round(per_step[-1], 3)},
         "roofline": roofline,
