@@ -405,6 +405,7 @@ template <class E, int BM, int BN, int AL, int BL, int KIND, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mlp_gemm(const KArgs g) {
   __shared__ __attribute__((aligned(16))) char smem[Geometry<E, BM, BN, AL, BL>::LDS];
+  if constexpr (KIND == GATEUP) clear_counters(g);
   gemm_tile<E, BM, BN, AL, BL, KIND>(g, smem, blockIdx.x, blockIdx.z);
 }
 
@@ -1195,6 +1196,24 @@ __device__ __forceinline__ void stream_store(const KArgs& g, int m, int n, const
   }
 }
 
+// fp32 partials of the split no-grad down projection: 16 bytes per lane with
+// the device-scope cache policy (sc1: the access bypasses this XCD's
+// non-coherent caches, as the compiler's own agent-scope atomic loads and
+// stores do), so one workgroup's stores are visible to the workgroup of
+// another XCD that adds them up. `plane` is one [T, N] plane; offsets stay
+// below 2^31 for T <= 128 and N within the shape limit.
+constexpr int kCoherentPolicy = 16;
+__device__ __forceinline__ void store_partial(const float* plane, int T, int N, int m, int n, f32x4_t v) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(plane, (int64_t)T * N * 4);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, ((uint32_t)m * N + n) * 4u, 0,
+                                         kCoherentPolicy);
+}
+__device__ __forceinline__ f32x4_t load_partial(const float* plane, int T, int N, int m, int n) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(plane, (int64_t)T * N * 4);
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, ((uint32_t)m * N + n) * 4u, 0,
+                                                                           kCoherentPolicy));
+}
+
 template <class E, int KIND, int MT>
 __global__ void __launch_bounds__(256) stream_gemm(const KArgs g, float* P, int splits, unsigned* ctr) {
   using namespace stream;
@@ -1337,24 +1356,19 @@ __global__ void __launch_bounds__(256) stream_gemm(const KArgs g, float* P, int 
         for (int v = 0; v < W; ++v) sum += *(const f32x4_t*)(lds + v * (NB * 1024) + (blk * 64 + lane) * 16);
         const int w = blk / MT, t = blk % MT;
         const int m = t * 16 + (lane & 15);
-        if (m < T && n < N) {
-          // device-coherent stores (they bypass this XCD's L2), read back by
-          // another workgroup of the unit
-          float* q = P + (((int64_t)split * NW + w) * T + m) * N + n;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) __hip_atomic_store(q + e, sum[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (m < T && n < N) store_partial(P + ((int64_t)split * NW + w) * T * N, T, N, m, n, sum);
       }
     }
   }
   if (direct) return;
 
-  // Arrival. The partials went out as device-coherent stores; each wave
-  // waits until its own have completed, the barrier then orders all of them
-  // before thread 0's atomic add on the unit's counter. The workgroup that
-  // brings the count to `splits` is the last: it reads the partials with
-  // device-coherent loads, so no cache of its CU or XCD can serve stale
-  // data, and no cache write-back or invalidation is needed anywhere.
+  // Arrival. The partials went out as device-coherent stores
+  // (store_partial); each wave waits until its own have completed, the
+  // barrier then orders all of them before thread 0's atomic add on the
+  // unit's counter. The workgroup that brings the count to `splits` is the
+  // last: it reads the partials with device-coherent loads, so no cache of
+  // its CU or XCD can serve stale data, and no cache write-back or
+  // invalidation is needed anywhere.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // (also: every wave is done reading the LDS sums)
   int* last_arrival = (int*)lds;
@@ -1372,11 +1386,7 @@ __global__ void __launch_bounds__(256) stream_gemm(const KArgs g, float* P, int 
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       sum[w] = f32x4_t{};
-      for (int sp = 0; sp < splits; ++sp) {
-        float* q = P + (((int64_t)sp * NW + w) * T + m) * N + n;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum[w][e] += __hip_atomic_load(q + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      for (int sp = 0; sp < splits; ++sp) sum[w] += load_partial(P + ((int64_t)sp * NW + w) * T * N, T, N, m, n);
     }
     stream_store<E, KIND>(g, m, n, sum);
   }
@@ -1547,10 +1557,7 @@ __global__ void __launch_bounds__(256) stream_ring(const KArgs g, float* P, int 
         int m, n;
         out_at(c, t, m, n);
         if (m >= T || n >= N) continue;
-        float* q = P + (((int64_t)split * NW + w) * T + m) * N + n;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __hip_atomic_store(q + e, acc[w][c][t][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_partial(P + ((int64_t)split * NW + w) * T * N, T, N, m, n, acc[w][c][t]);
       }
   // arrival, as in stream_gemm: device-coherent partials, each wave waits
   // for its own stores, the barrier orders them before the atomic add
@@ -1570,11 +1577,7 @@ __global__ void __launch_bounds__(256) stream_ring(const KArgs g, float* P, int 
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       sum[w] = f32x4_t{};
-      for (int sp = 0; sp < splits; ++sp) {
-        float* q = P + (((int64_t)sp * NW + w) * T + m) * N + n;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum[w][e] += __hip_atomic_load(q + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      for (int sp = 0; sp < splits; ++sp) sum[w] += load_partial(P + ((int64_t)sp * NW + w) * T * N, T, N, m, n);
     }
     stream_store<E, KIND>(g, m, n, sum);
   }
@@ -1847,6 +1850,9 @@ constexpr int kInferPartialCap = 2;
 // D = 4096, H = 11008, S = 256: 124 us there, 184 us unsplit streaming,
 // 104 us split three ways (with 2.6 (A + Y) of memory).
 constexpr int kInferSplitMaxT = 128;
+// Tokens up to which the no-grad gate/up streams whatever H (few tokens:
+// the few-token kernel or the per-wave rings).
+constexpr int kInferGateSkinnyT = 128;
 
 // No-grad workspace. The A plane [T, H]; for 16-bit with T <= kInferSplitMaxT
 // also the down projection's arrival counters (one per 64 columns) and, when
@@ -1856,7 +1862,7 @@ constexpr int kInferSplitMaxT = 128;
 // weight-streaming kernels.
 struct InferPlan {
   size_t a_bytes = 0, ctr_off = 0, p_off = 0, total = 0;
-  bool stream = false, down_stream = false;
+  bool stream = false, down_stream = false;  // gate/up, down on the weight-streaming kernels
   int down_units = 0, down_splits = 1;
 };
 static inline InferPlan infer_plan(int64_t T, int64_t D, int64_t H, size_t e) {
@@ -1864,11 +1870,10 @@ static inline InferPlan infer_plan(int64_t T, int64_t D, int64_t H, size_t e) {
   p.a_bytes = (size_t)T * H * e;
   p.total = p.a_bytes;
   if (e != 2 || T <= 0 || !stream_t(T)) return p;
-  // above kInferSplitMaxT tokens the gate/up streams only with at least 128
-  // units of 64 hidden units (H = 2816, S = 256: 33 us streaming on 44
+  // above kInferGateSkinnyT tokens the gate/up streams only with at least
+  // 128 units of 64 hidden units (H = 2816, S = 256: 33 us streaming on 44
   // units, 24 us on the 64-row tile engine; H = 11008: 103 us against 148)
-  if (T > kInferSplitMaxT && cdiv(H, stream::NC) < 128) return p;
-  p.stream = true;
+  p.stream = T <= kInferGateSkinnyT || cdiv(H, stream::NC) >= 128;
   if (T > kInferSplitMaxT) return p;
   p.down_stream = true;
   p.down_units = cdiv(D, stream::NC);
@@ -2156,24 +2161,17 @@ int run_infer(const void* X, const void* Wg, const void* Wu, const void* Wd, voi
   char* Ap = (char*)ws;
   const InferPlan pl = infer_plan(T, D, H, E::kBytes);
   const StreamArgs sg{1, nullptr, nullptr};
-  if (LIN || !pl.stream) {
-    int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, nullptr, s);
-    if (rc) return rc;
-    return Pa::template down<7>(Ap, Wd, Y, T, D, H, nullptr, s);
-  }
-  if (!pl.down_stream) {
-    // above kInferSplitMaxT tokens an unsplit streaming down projection
-    // reads all of A once per 64 columns: the 64-row tile engine is faster
-    int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, &sg, s);
-    if (rc) return rc;
-    return Pa::template down<7>(Ap, Wd, Y, T, D, H, nullptr, s);
-  }
-  unsigned* ctr = (unsigned*)(Ap + pl.ctr_off);
-  const StreamArgs sd{pl.down_splits, pl.down_splits > 1 ? (float*)(Ap + pl.p_off) : nullptr, ctr};
-  int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, &sg, s, ctr,
-                                  pl.down_units);
+  const bool gs = !LIN && pl.stream, ds = !LIN && pl.down_stream;
+  // the gate/up launch (streaming or not) clears the down launch's counters
+  unsigned* ctr = ds ? (unsigned*)(Ap + pl.ctr_off) : nullptr;
+  int rc = Pa::template gateup<6>(X, Wg, Wu, Ap, nullptr, nullptr, T, D, H, false, two_round, gs ? &sg : nullptr, s,
+                                  ctr, ds ? pl.down_units : 0);
   if (rc) return rc;
-  return Pa::template down<7>(Ap, Wd, Y, T, D, H, &sd, s);
+  // above kInferSplitMaxT tokens an unsplit streaming down projection reads
+  // all of A once per 64 columns: the 64-row tile engine is faster there
+  const StreamArgs sd{pl.down_splits, pl.down_splits > 1 ? (float*)(Ap + pl.p_off) : nullptr, ctr};
+  return Pa::template down<7>(Ap, Wd, Y, T, D, H, ds ? &sd : nullptr, s);
 }
+
 
 }  // namespace swiglu
