@@ -288,8 +288,10 @@ def infer_sweep(mlp, torch, dev, reps=20, copy_gbps=None):
     Also the host-inclusive wall time of one call (Python binding, argument
     checks, the launches, completion), eagerly and as a replay of a HIP graph
     that captured the same call (checked bitwise against the eager output),
-    measured alternately after warm-up replays, and the intermediate memory
-    of the call (workspace + Y) beside A + Y."""
+    measured alternately after warm-up replays; the same per call for eight
+    calls back to back (eagerly, and as one graph of all eight: a decode
+    step through eight layers); and the intermediate memory of the call
+    (workspace + Y) beside A + Y."""
     from synth import INFER_DH, INFER_S, make_inputs
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -346,6 +348,25 @@ def infer_sweep(mlp, torch, dev, reps=20, copy_gbps=None):
                     torch.cuda.synchronize()
                     ts.append((time.perf_counter() - t0) * 1e6)
             del graph
+            # eight calls back to back (a decode step through eight layers):
+            # eager, and replayed from one graph that captured all eight
+            g8 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g8):
+                for _ in range(8):
+                    mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws)
+            for _ in range(3):
+                g8.replay()
+            eager8 = lambda: [mlp.infer(X, Wg, Wu, Wd, y=y, workspace=ws) for _ in range(8)]
+            t_e8, t_g8 = [], []
+            for _ in range(reps // 2):
+                for call, ts in ((eager8, t_e8), (g8.replay, t_g8)):
+                    flush.sum()
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    call()
+                    torch.cuda.synchronize()
+                    ts.append((time.perf_counter() - t0) * 1e6 / 8)
+            del g8
             gbps = nbytes / (med * 1e-6) / 1e9
             a_y = 2 * S * (H + D)
             inter = ws.numel() + 2 * S * D
@@ -355,6 +376,8 @@ def infer_sweep(mlp, torch, dev, reps=20, copy_gbps=None):
                             "wall_us_eager": round(sorted(t_e)[reps // 2], 1),
                             "wall_us_graph": round(sorted(t_g)[reps // 2], 1),
                             "graph_bitwise_equal": same,
+                            "wall_us_per_call_8_eager": round(sorted(t_e8)[len(t_e8) // 2], 1),
+                            "wall_us_per_call_8_graph": round(sorted(t_g8)[len(t_g8) // 2], 1),
                             "intermediate_MiB": round(inter / 2**20, 3),
                             "intermediate_over_A_plus_Y": round(inter / a_y, 3)}
         out[f"{D}x{H}"] = rows

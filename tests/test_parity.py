@@ -270,3 +270,25 @@ def test_zero_tokens(mlp):
     assert dx.shape == (0, 64)
     assert not dwg.any() and not dwu.any() and not dwd.any()
     assert mlp.infer(g["X"], g["Wg"], g["Wu"], g["Wd"]).shape == (0, 64)
+
+
+@pytest.mark.parametrize("D,H", [(1024, 2816), (4096, 11008)])
+def test_no_grad_workspace_contents_do_not_matter(mlp, D, H):
+    """The no-grad workspace holds the down projection's arrival counters and
+    partials; its contents on entry must not matter (the gate/up launch
+    clears the counters). A workspace filled with 0xFF bytes, and one reused
+    across shapes and splits, give the same bits as a fresh one."""
+    wts = make_inputs(1, D, H, seed=5150 + D, dtype="bf16", with_dy=False)
+    Wg, Wu, Wd = (wts[k].cuda() for k in ("Wg", "Wu", "Wd"))
+    big = torch.empty(mlp.infer_workspace_bytes(128, D, H), dtype=torch.uint8, device="cuda")
+    for S in (128, 7, 64, 1, 100):
+        X = make_inputs(S, D, H, seed=S + 11, dtype="bf16", with_dy=False)["X"].cuda()
+        n = mlp.infer_workspace_bytes(S, D, H)
+        fresh = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        y0 = mlp.infer(X, Wg, Wu, Wd, workspace=fresh)
+        junk = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+        y1 = mlp.infer(X, Wg, Wu, Wd, workspace=junk)
+        y2 = mlp.infer(X, Wg, Wu, Wd, workspace=big[:n])  # reused from the previous shape
+        torch.cuda.synchronize()
+        banner(f"workspace contents D={D} S={S}")
+        assert torch.equal(y0, y1) and torch.equal(y0, y2), (D, S)
