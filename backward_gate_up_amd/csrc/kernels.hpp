@@ -438,6 +438,10 @@ mlp_gemm_pair(const KArgs g1, const KArgs g2) {
 // A wave's output block is `rows` x W elements (W = 64 or 128); in LDS row r
 // holds W*2 bytes and its 16-byte chunk c sits at chunk c ^ (r % (W/8)).
 // ---------------------------------------------------------------------------
+// Cache-policy operand of the buffer store builtins that selects the
+// non-temporal (nt) hint on gfx950.
+constexpr int kNonTemporalPolicy = 2;
+
 template <class E, int W>
 struct WaveBlock {
   static constexpr int NC = W / 8;       // 16-byte chunks per row
@@ -453,19 +457,49 @@ struct WaveBlock {
   __device__ __forceinline__ typename E::vec4 get4(int r, int col) const {
     return *(const typename E::vec4*)(buf + off(r, col));
   }
-  // store rows [0, rows) to dst(row0 + r, col0 + c), masked to M x N
-  __device__ __forceinline__ void store(char* dst, int64_t ld, int row0, int col0, int M, int N, int rows,
-                                        int lane) const {
-    const int n16 = rows * NC;
-#pragma unroll 4
-    for (int g = lane; g < n16; g += 64) {
-      const int r = g / NC, c = g % NC;
-      const u32x4_t v = *(const u32x4_t*)(buf + r * RB + ((c ^ (r & (NC - 1))) << 4));
-      const int gr = row0 + r, gc = col0 + c * 8;
-      // non-temporal: results are not re-read by this kernel, and streaming
-      // them past L2 leaves it to the operand tiles (gate/up writes three
-      // [T, H] planes: measured 2.5-4 % faster, the other stages unchanged)
-      if (gr < M && gc < N) __builtin_nontemporal_store(v, (u32x4_t*)(dst + ((int64_t)gr * ld + gc) * 2));
+  // Row chunks i = b .. b + NB - 1 of this lane (chunk i covers 16-byte
+  // chunk (i * 64 + lane) % NC of row (i * 64 + lane) / NC), read from LDS
+  // back to back so that one LDS latency covers the batch.
+  template <int NB>
+  __device__ __forceinline__ void read_chunks(u32x4_t (&v)[NB], int b, int lane) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int g = (b + i) * 64 + lane, r = g / NC, c = g % NC;
+      v[i] = *(const u32x4_t*)(buf + r * RB + ((c ^ (r & (NC - 1))) << 4));
+    }
+  }
+  // Store those chunks to dst(row0 + r, col0 + c), masked to M x N. One
+  // store instruction per chunk, whatever the mask: chunks outside the
+  // matrix take an offset past the descriptor, which drops them, so a
+  // caller can count the stores in vmcnt. Non-temporal: results are not
+  // re-read by this kernel, and streaming them past L2 leaves it to the
+  // operand tiles (gate/up writes three [T, H] planes: measured 2.5-4 %
+  // faster, the other stages unchanged).
+  template <int NB>
+  __device__ __forceinline__ void write_chunks(const u32x4_t (&v)[NB], int b, char* dst, int64_t ld, int row0,
+                                               int col0, int M, int N, int lane) const {
+    const int64_t first = (int64_t)row0 * ld + col0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + first * 2, ((int64_t)M * ld - first) * 2);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int g = (b + i) * 64 + lane, r = g / NC, c = g % NC;
+      const bool in = row0 + r < M && col0 + c * 8 < N;
+      const uint32_t off = in ? (uint32_t)((r * (int)ld + c * 8) * 2) : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(v[i], rs, off, 0, kNonTemporalPolicy);
+    }
+  }
+  // store rows [0, ROWS) to dst(row0 + r, col0 + c), masked to M x N:
+  // ROWS * NC / 64 store instructions, in batches of up to eight chunks
+  template <int ROWS>
+  __device__ __forceinline__ void store(char* dst, int64_t ld, int row0, int col0, int M, int N, int lane) const {
+    constexpr int NI = ROWS * NC / 64;
+    constexpr int NB = NI < 8 ? NI : 8;
+    static_assert(NI % NB == 0, "whole batches");
+#pragma unroll
+    for (int b = 0; b < NI; b += NB) {
+      u32x4_t v[NB];
+      read_chunks<NB>(v, b, lane);
+      write_chunks<NB>(v, b, dst, ld, row0, col0, M, N, lane);
     }
   }
   // load rows [0, rows) from src(row0 + r, col0 + c) with direct-to-LDS
@@ -524,9 +558,9 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
     };
     if (g.two_round) stage_ag(std::true_type{});
     else stage_ag(std::false_type{});
-    pa.store(g.c0, g.ldc, r0, c0, g.M, g.N, 128, lane);
+    pa.template store<128>(g.c0, g.ldc, r0, c0, g.M, g.N, lane);
     if (g.store_gu) {
-      pg.store(g.c1, g.ldc, r0, c0, g.M, g.N, 128, lane);
+      pg.template store<128>(g.c1, g.ldc, r0, c0, g.M, g.N, lane);
       WaveBlock<E, 64> pu{wbuf};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -539,7 +573,7 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
             for (int e = 0; e < 4; ++e) uv[e] = E::from_f32(acc[i][j + 2][q * 4 + e]);
             pu.put4(i * 32 + ml, j * 32 + q * 8 + nl, uv);
           }
-      pu.store(g.c2, g.ldc, r0, c0, g.M, g.N, 128, lane);
+      pu.template store<128>(g.c2, g.ldc, r0, c0, g.M, g.N, lane);
     }
   } else if constexpr (KIND == DSWIGLU) {
     // wave block: 128 rows x 128 hidden units, in four quarters of 32 rows
@@ -547,11 +581,13 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
     // into LDS, turned into dG and dU in place (this tile's own (t, h) block
     // only) and stored back. Two LDS slots of 16 KiB: the loads of quarter
     // q + 1 are in flight while quarter q is computed and stored, and those
-    // of q + 2 reuse q's slot once its stores have read it. vmcnt counts
-    // this wave's loads and stores in issue order: [loads 0] [loads 1]
-    // [stores 0] [loads 2] [stores 1] [loads 3] [stores 2] ... A quarter's
-    // stores may be fewer than 16 instructions (rows past M are skipped), so
-    // each wait lets only the 16 loads issued last stay outstanding.
+    // of q + 2 go into q's slot as soon as q's results have been read back
+    // into registers, before q's stores. A quarter is 16 loads (8 per plane)
+    // and 16 stores (8 per plane, out-of-range chunks dropped by the
+    // descriptor rather than skipped), and vmcnt counts this wave's loads and
+    // stores in issue order: L0 L1 | L2 S0 | L3 S1 | S2 | S3. So waiting for
+    // the loads of quarter q never waits for a store: 16, 32, 48 and 32
+    // operations issued after them may stay outstanding.
     const int64_t plane_bytes = (int64_t)g.M * g.ldc * 2;
     const int c0 = n0 + wn * 128;
     auto issue = [&](int q) {
@@ -564,22 +600,32 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
     issue(1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (q < 3) ring::wait_vmcnt<16>();  // loads of q + 1 may stay in flight
-      else ring::wait_vmcnt<0>();
+      if (q == 0) ring::wait_vmcnt<16>();
+      else if (q == 2) ring::wait_vmcnt<48>();
+      else ring::wait_vmcnt<32>();
       WaveBlock<E, 128> pg{wbuf + (q & 1) * 16384}, pu{wbuf + (q & 1) * 16384 + 8192};
+      // every G and U value of the quarter first (one LDS latency), then
+      // the math
+      V4 gv[4][4], uv[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          gv[j][qq] = pg.get4(ml, j * 32 + qq * 8 + nl);
+          uv[j][qq] = pu.get4(ml, j * 32 + qq * 8 + nl);
+        }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int r = ml, c = j * 32 + qq * 8 + nl;
-          const V4 gv = pg.get4(r, c), uv = pu.get4(r, c);
           V4 dg, du;
           float da[4], gf[4], uf[4], dgf[4], duf[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             da[e] = acc[q][j][qq * 4 + e];
-            gf[e] = E::to_f32(gv[e]);
-            uf[e] = E::to_f32(uv[e]);
+            gf[e] = E::to_f32(gv[j][qq][e]);
+            uf[e] = E::to_f32(uv[j][qq][e]);
           }
           dswiglu4<E>(da, gf, uf, dgf, duf);
 #pragma unroll
@@ -590,10 +636,15 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
           pg.put4(r, c, dg);
           pu.put4(r, c, du);
         }
-      const int r0 = m0 + wm * 128 + q * 32;
-      pg.store(g.c0, g.ldc, r0, c0, g.M, g.N, 32, lane);
-      pu.store(g.c1, g.ldc, r0, c0, g.M, g.N, 32, lane);
+      u32x4_t vg[8], vu[8];
+      pg.template read_chunks<8>(vg, 0, lane);
+      pu.template read_chunks<8>(vu, 0, lane);
+      // the slot's contents are in registers: quarter q + 2 may load into it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (q + 2 < 4) issue(q + 2);
+      const int r0 = m0 + wm * 128 + q * 32;
+      pg.template write_chunks<8>(vg, 0, g.c0, g.ldc, r0, c0, g.M, g.N, lane);
+      pu.template write_chunks<8>(vu, 0, g.c1, g.ldc, r0, c0, g.M, g.N, lane);
     }
   } else {
     // PLAIN / DX: 128 x 128 block of C
@@ -609,7 +660,7 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
           for (int e = 0; e < 4; ++e) v[e] = E::from_f32(acc[i][j][q * 4 + e]);
           pc.put4(i * 32 + ml, j * 32 + q * 8 + nl, v);
         }
-    pc.store(C, g.ldc, m0 + wm * 128, n0 + wn * 128, g.M, g.N, 128, lane);
+    pc.template store<128>(C, g.ldc, m0 + wm * 128, n0 + wn * 128, g.M, g.N, lane);
   }
 }
 
