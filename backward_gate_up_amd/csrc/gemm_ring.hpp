@@ -110,13 +110,22 @@ struct Dma {
     }
   }
 
+  // Descriptor of a KC operand's rows [r0, op.rows). It does not change
+  // along K, so a tile builds it once, not at every stage.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t kc_rsrc(const Operand& op, int r0) {
+    return make_rsrc(op.base + (int64_t)r0 * op.ld * 2, ((int64_t)(op.rows - r0)) * op.ld * 2);
+  }
+
   // KC: rows [r0, r0 + 256), K columns [k0, k0 + BKT) into `tile`; this
   // wave's pieces j0 .. j1 - 1.
   __device__ __forceinline__ void issue_kc(const Operand& op, int r0, int k0, char* tile, int wave, int lane,
                                            int j0 = 0, int j1 = G::PPW) {
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(op.base + (int64_t)r0 * op.ld * 2, ((int64_t)(op.rows - r0)) * op.ld * 2);
-    const bool tail = k0 + BKT > op.k;
+    issue_kc(kc_rsrc(op, r0), op.k, k0, tile, wave, lane, j0, j1);
+  }
+  // The same from the tile's descriptor `rs` of an operand with K = kk.
+  __device__ __forceinline__ void issue_kc(const __amdgpu_buffer_rsrc_t rs, int kk, int k0, char* tile, int wave,
+                                           int lane, int j0 = 0, int j1 = G::PPW) {
+    const bool tail = k0 + BKT > kk;
 #pragma unroll
     for (int j = 0; j < G::PPW; ++j) {
       if (j < j0 || j >= j1) continue;
@@ -125,9 +134,46 @@ struct Dma {
       if (tail) {
         const int r = q * G::RPI + lane / G::LPR;
         const int c = (lane % G::LPR) ^ kc_swz<BKT>(r);
-        if (k0 + c * 8 >= op.k) vo = kOOB;
+        if (k0 + c * 8 >= kk) vo = kOOB;
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + q * 1024), 16, vo, k0 * 2, 0, 0);
+    }
+  }
+
+  // An M/N-major operand as this wave reads it (waves 0-1: columns from c0
+  // of op0, waves 2-3: from c1 of op1), built once per tile so that a stage
+  // costs one multiply-add for its base and, only on the stage that reaches
+  // the last K row, the exact size of the descriptor.
+  struct McSrc {
+    const char* base;  // K row 0, column cs
+    int64_t rowb;      // bytes per K row
+    int kk;            // K rows
+    int cs2;           // cs in bytes
+  };
+  __device__ __forceinline__ static McSrc mc_src(const Operand& op0, int c0, const Operand& op1, int c1,
+                                                 int wave) {
+    const bool second = wave >= 2;
+    const Operand& op = second ? op1 : op0;
+    const int cs = second ? c1 : c0;
+    return McSrc{op.base + (int64_t)cs * 2, op.ld * 2, op.k, cs * 2};
+  }
+  // K rows [k0, k0 + BKT) of the wave's sub-tile. A stage that ends before
+  // the last K row gets BKT rows of descriptor (its reads past column N, if
+  // any, land in the next row, which exists); the stage that reaches it gets
+  // exactly the bytes up to the end of K row kk - 1, so rows past K read as
+  // zeros and nothing past the matrix is touched. BKT rows of the leading
+  // dimension stay below 2^31 bytes (the shape limit), so the size is int32.
+  __device__ __forceinline__ void issue_mcs(const McSrc& m, int k0, char* tile, int wave, int j0 = 0,
+                                           int j1 = G::PPW) {
+    const int rb = (int)m.rowb;
+    int n = k0 + BKT < m.kk ? BKT * rb : (m.kk - k0) * rb - m.cs2;
+    n = n < 0 ? 0 : n;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc32(m.base + (int64_t)k0 * m.rowb, n);
+#pragma unroll
+    for (int j = 0; j < G::PPW; ++j) {
+      if (j < j0 || j >= j1) continue;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (wave * G::PPW + j) * 1024), 16, voff[j],
+                                               0, 0, 0);
     }
   }
 

@@ -98,6 +98,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
   int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : (bytes < 0 ? 0 : (int32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcWord3);
 }
+// The same for a size already known to lie in [0, 2^31).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void* p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, kRsrcWord3);
+}
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 

@@ -714,29 +714,54 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   const int nk = (KIND == DX) ? 2 * nk1 : (split ? (nk1 - sb < g.kchunk ? nk1 - sb : g.kchunk) : nk1);
   char* st[4] = {st0, st1, st2, st3};
 
+  // descriptors (K-major) and M/N-major sources built once per tile: [0]
+  // the operand (DX: its first half, (dG, Wg)), [1] DX's second half
+  using DA = Dma<AL>;
+  using DB = Dma<BL>;
+  __amdgpu_buffer_rsrc_t ra[2], rb[2];
+  typename DA::McSrc ma[2];
+  typename DB::McSrc mb[2];
+  if constexpr (AL == KC) {
+    ra[0] = DA::kc_rsrc(KIND == DX ? g.a0 : A, m0);
+    ra[1] = KIND == DX ? DA::kc_rsrc(g.a1, m0) : ra[0];
+  } else {
+    ma[0] = DA::mc_src(A, m0, A, m0 + 128, wave);
+  }
+  if constexpr (BL == KC) {
+    // gate/up: B rows [0, 128) from Wg (waves 0-1), [128, 256) from Wu
+    const Operand& b0 = (KIND == GATEUP && wave >= 2) ? g.b1 : (KIND == DX ? g.b0 : B);
+    rb[0] = DB::kc_rsrc(b0, n0);
+    rb[1] = KIND == DX ? DB::kc_rsrc(g.b1, n0) : rb[0];
+  } else if constexpr (KIND == GATEUP) {
+    mb[0] = DB::mc_src(g.b0, n0, g.b1, n0, wave);
+  } else if constexpr (KIND == DX) {
+    mb[0] = DB::mc_src(g.b0, n0, g.b0, n0 + 128, wave);
+    mb[1] = DB::mc_src(g.b1, n0, g.b1, n0 + 128, wave);
+  } else {
+    mb[0] = DB::mc_src(B, n0, B, n0 + 128, wave);
+  }
+
   auto issue_a = [&](int s, char* stg) {
     if constexpr (KIND == DX) {
       const bool h = s >= nk1;
-      da.issue_kc(h ? g.a1 : g.a0, m0, (h ? s - nk1 : s) * BK, stg, wave, lane);
+      da.issue_kc(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK, stg, wave, lane);
     } else if constexpr (AL == KC) {
-      da.issue_kc(A, m0, (sb + s) * BK, stg, wave, lane);
+      da.issue_kc(ra[0], A.k, (sb + s) * BK, stg, wave, lane);
     } else {
-      da.issue_mc(A, m0, A, m0 + 128, (sb + s) * BK, stg, wave);
+      da.issue_mcs(ma[0], (sb + s) * BK, stg, wave);
     }
   };
   auto issue_b = [&](int s, char* stg) {
     if constexpr (KIND == DX) {
       const bool h = s >= nk1;
-      const Operand& op = h ? g.b1 : g.b0;
-      if constexpr (BL == KC) db.issue_kc(op, n0, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
-      else db.issue_mc(op, n0, op, n0 + 128, (h ? s - nk1 : s) * BK, stg + OPB, wave);
-    } else if constexpr (KIND == GATEUP) {
-      if constexpr (BL == KC) db.issue_kc(wave >= 2 ? g.b1 : g.b0, n0, s * BK, stg + OPB, wave, lane);
-      else db.issue_mc(g.b0, n0, g.b1, n0, s * BK, stg + OPB, wave);
+      if constexpr (BL == KC)
+        db.issue_kc(h ? rb[1] : rb[0], h ? g.b1.k : g.b0.k, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
+      else db.issue_mcs(h ? mb[1] : mb[0], (h ? s - nk1 : s) * BK, stg + OPB, wave);
     } else if constexpr (BL == KC) {
-      db.issue_kc(B, n0, (sb + s) * BK, stg + OPB, wave, lane);
+      db.issue_kc(rb[0], KIND == GATEUP ? (wave >= 2 ? g.b1.k : g.b0.k) : B.k, (sb + s) * BK, stg + OPB, wave,
+                  lane);
     } else {
-      db.issue_mc(B, n0, B, n0 + 128, (sb + s) * BK, stg + OPB, wave);
+      db.issue_mcs(mb[0], (sb + s) * BK, stg + OPB, wave);
     }
   };
   auto issue = [&](int s, char* stg) {
@@ -872,14 +897,29 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
   const int nk1 = (A.k + BK2 - 1) / BK2;
   const int nk = (KIND == DX) ? 2 * nk1 : nk1;
   constexpr int NT = Geo<BK2>::PPW;  // loads per wave per operand tile
+  // K-major descriptors, built once per tile: [0] the operand (DX: its first
+  // half, (dG, Wg)), [1] DX's second half (dU, Wu)
+  using DA = Dma<AL, BK2>;
+  using DB = Dma<BL, BK2>;
+  __amdgpu_buffer_rsrc_t ra[2], rb[2];
+  if constexpr (AL == KC) {
+    ra[0] = DA::kc_rsrc(KIND == DX ? g.a0 : A, m0);
+    ra[1] = KIND == DX ? DA::kc_rsrc(g.a1, m0) : ra[0];
+  }
+  if constexpr (BL == KC) {
+    // gate/up: B rows [0, 128) from Wg (waves 0-1), [128, 256) from Wu
+    const Operand& b0 = (KIND == GATEUP && wave >= 2) ? g.b1 : (KIND == DX ? g.b0 : B);
+    rb[0] = DB::kc_rsrc(b0, n0);
+    rb[1] = KIND == DX ? DB::kc_rsrc(g.b1, n0) : rb[0];
+  }
 
   // pieces [j0, j1) of this wave's share of A of stage s
   auto issue_a = [&](int s, char* t, int j0 = 0, int j1 = NT) {
     if constexpr (KIND == DX) {
       const bool h = s >= nk1;
-      da.issue_kc(h ? g.a1 : g.a0, m0, (h ? s - nk1 : s) * BK2, t, wave, lane, j0, j1);
+      da.issue_kc(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK2, t, wave, lane, j0, j1);
     } else if constexpr (AL == KC) {
-      da.issue_kc(A, m0, s * BK2, t, wave, lane, j0, j1);
+      da.issue_kc(ra[0], A.k, s * BK2, t, wave, lane, j0, j1);
     } else {
       da.issue_mc(A, m0, A, m0 + 128, s * BK2, t, wave, j0, j1);
     }
@@ -888,13 +928,13 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
     if constexpr (KIND == DX) {
       const bool h = s >= nk1;
       const Operand& op = h ? g.b1 : g.b0;
-      if constexpr (BL == KC) db.issue_kc(op, n0, (h ? s - nk1 : s) * BK2, t, wave, lane);
+      if constexpr (BL == KC) db.issue_kc(h ? rb[1] : rb[0], op.k, (h ? s - nk1 : s) * BK2, t, wave, lane);
       else db.issue_mc(op, n0, op, n0 + 128, (h ? s - nk1 : s) * BK2, t, wave);
     } else if constexpr (KIND == GATEUP) {
-      if constexpr (BL == KC) db.issue_kc(wave >= 2 ? g.b1 : g.b0, n0, s * BK2, t, wave, lane);
+      if constexpr (BL == KC) db.issue_kc(rb[0], (wave >= 2 ? g.b1 : g.b0).k, s * BK2, t, wave, lane);
       else db.issue_mc(g.b0, n0, g.b1, n0, s * BK2, t, wave);
     } else if constexpr (BL == KC) {
-      db.issue_kc(B, n0, s * BK2, t, wave, lane);
+      db.issue_kc(rb[0], B.k, s * BK2, t, wave, lane);
     } else {
       db.issue_mc(B, n0, B, n0 + 128, s * BK2, t, wave);
     }
