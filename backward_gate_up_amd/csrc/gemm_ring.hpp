@@ -120,12 +120,15 @@ struct Dma {
   // wave's pieces j0 .. j1 - 1.
   __device__ __forceinline__ void issue_kc(const Operand& op, int r0, int k0, char* tile, int wave, int lane,
                                            int j0 = 0, int j1 = G::PPW) {
-    issue_kc(kc_rsrc(op, r0), op.k, k0, tile, wave, lane, j0, j1);
+    issue_kcr<true>(kc_rsrc(op, r0), op.k, k0, tile, wave, lane, j0, j1);
   }
   // The same from the tile's descriptor `rs` of an operand with K = kk.
-  __device__ __forceinline__ void issue_kc(const __amdgpu_buffer_rsrc_t rs, int kk, int k0, char* tile, int wave,
-                                           int lane, int j0 = 0, int j1 = G::PPW) {
-    const bool tail = k0 + BKT > kk;
+  // KT = false: K is a multiple of BKT, so no stage has a K tail and the
+  // per-chunk check is compiled out.
+  template <bool KT>
+  __device__ __forceinline__ void issue_kcr(const __amdgpu_buffer_rsrc_t rs, int kk, int k0, char* tile, int wave,
+                                            int lane, int j0 = 0, int j1 = G::PPW) {
+    const bool tail = KT && k0 + BKT > kk;
 #pragma unroll
     for (int j = 0; j < G::PPW; ++j) {
       if (j < j0 || j >= j1) continue;

@@ -741,90 +741,98 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
     mb[0] = DB::mc_src(B, n0, B, n0 + 128, wave);
   }
 
-  auto issue_a = [&](int s, char* stg) {
-    if constexpr (KIND == DX) {
-      const bool h = s >= nk1;
-      da.issue_kc(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK, stg, wave, lane);
-    } else if constexpr (AL == KC) {
-      da.issue_kc(ra[0], A.k, (sb + s) * BK, stg, wave, lane);
-    } else {
-      da.issue_mcs(ma[0], (sb + s) * BK, stg, wave);
-    }
-  };
-  auto issue_b = [&](int s, char* stg) {
-    if constexpr (KIND == DX) {
-      const bool h = s >= nk1;
-      if constexpr (BL == KC)
-        db.issue_kc(h ? rb[1] : rb[0], h ? g.b1.k : g.b0.k, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
-      else db.issue_mcs(h ? mb[1] : mb[0], (h ? s - nk1 : s) * BK, stg + OPB, wave);
-    } else if constexpr (BL == KC) {
-      db.issue_kc(rb[0], KIND == GATEUP ? (wave >= 2 ? g.b1.k : g.b0.k) : B.k, (sb + s) * BK, stg + OPB, wave,
-                  lane);
-    } else {
-      db.issue_mcs(mb[0], (sb + s) * BK, stg + OPB, wave);
-    }
-  };
-  auto issue = [&](int s, char* stg) {
-    issue_a(s, stg);
-    issue_b(s, stg);
-  };
-
-  using F = RFrags<E, AL, BL>;
-  F f0, f1;
-  if (nk > 0) {
-    issue(0, st0);
-    if (nk > 1) issue(1, st1);
-    if (nk > 2) issue(2, st2);
-    if (nk > 2) wait_vmcnt<2 * L>();
-    else if (nk > 1) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    f0.read(st0, a_rows, b_rows, 0, lane);
-  }
-  // Steady state: four stages per trip with static ring slots, every stage
-  // issuing the loads of stage s + 3 (needs s + 6 < nk for the last one):
-  // its A tile during the first sub-step, its B tile during the second. At
-  // the wait, A and B of stage s + 2 and A of stage s + 3 may still be in
-  // flight.
-  auto step = [&](int s, auto J) {
-    constexpr int j = decltype(J)::value;
-    issue_a(s + 3, st[(j + 3) & 3]);
-    f1.read(st[j], a_rows, b_rows, 1, lane);
-    f0.mma(acc);
-    interleave<F::kReads, L / 2>();
-    wait_vmcnt<L + L / 2>();
-    lds_barrier();
-    issue_b(s + 3, st[(j + 3) & 3]);
-    f0.read(st[(j + 1) & 3], a_rows, b_rows, 0, lane);
-    f1.mma(acc);
-    interleave<F::kReads, L / 2>();
-  };
-  int s = 0;
-  for (; s + 7 <= nk; s += 4) {
-    step(s, std::integral_constant<int, 0>{});
-    step(s + 1, std::integral_constant<int, 1>{});
-    step(s + 2, std::integral_constant<int, 2>{});
-    step(s + 3, std::integral_constant<int, 3>{});
-  }
-  // Last stages: same order with run-time slot selection and counts.
   auto slot = [&](int i) -> char* {
     i &= 3;
     return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3;
   };
-  for (; s < nk; ++s) {
-    if (s + 3 < nk) issue(s + 3, slot(s + 3));
-    f1.read(slot(s), a_rows, b_rows, 1, lane);
-    f0.mma(acc);
-    if (s + 1 < nk) {
-      const int later = nk - (s + 2) < 2 ? nk - (s + 2) : 2;  // stages issued after s + 1
-      if (later >= 2) wait_vmcnt<2 * L>();
-      else if (later == 1) wait_vmcnt<L>();
+  // The K loop, compiled with (KT) and without the K-tail checks of K-major
+  // loads; the epilogue after it exists once.
+  auto kloop = [&](auto KTc) {
+    constexpr bool KT = decltype(KTc)::value;
+    auto issue_a = [&](int s, char* stg) {
+      if constexpr (KIND == DX) {
+        const bool h = s >= nk1;
+        da.template issue_kcr<KT>(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK, stg, wave, lane);
+      } else if constexpr (AL == KC) {
+        da.template issue_kcr<KT>(ra[0], A.k, (sb + s) * BK, stg, wave, lane);
+      } else {
+        da.issue_mcs(ma[0], (sb + s) * BK, stg, wave);
+      }
+    };
+    auto issue_b = [&](int s, char* stg) {
+      if constexpr (KIND == DX) {
+        const bool h = s >= nk1;
+        if constexpr (BL == KC)
+          db.template issue_kcr<KT>(h ? rb[1] : rb[0], h ? g.b1.k : g.b0.k, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
+        else db.issue_mcs(h ? mb[1] : mb[0], (h ? s - nk1 : s) * BK, stg + OPB, wave);
+      } else if constexpr (BL == KC) {
+        db.template issue_kcr<KT>(rb[0], KIND == GATEUP ? (wave >= 2 ? g.b1.k : g.b0.k) : B.k, (sb + s) * BK, stg + OPB, wave,
+                    lane);
+      } else {
+        db.issue_mcs(mb[0], (sb + s) * BK, stg + OPB, wave);
+      }
+    };
+    auto issue = [&](int s, char* stg) {
+      issue_a(s, stg);
+      issue_b(s, stg);
+    };
+
+    using F = RFrags<E, AL, BL>;
+    F f0, f1;
+    if (nk > 0) {
+      issue(0, st0);
+      if (nk > 1) issue(1, st1);
+      if (nk > 2) issue(2, st2);
+      if (nk > 2) wait_vmcnt<2 * L>();
+      else if (nk > 1) wait_vmcnt<L>();
       else wait_vmcnt<0>();
       lds_barrier();
-      f0.read(slot(s + 1), a_rows, b_rows, 0, lane);
+      f0.read(st0, a_rows, b_rows, 0, lane);
     }
-    f1.mma(acc);
-  }
+    // Steady state: four stages per trip with static ring slots, every stage
+    // issuing the loads of stage s + 3 (needs s + 6 < nk for the last one):
+    // its A tile during the first sub-step, its B tile during the second. At
+    // the wait, A and B of stage s + 2 and A of stage s + 3 may still be in
+    // flight.
+    auto step = [&](int s, auto J) {
+      constexpr int j = decltype(J)::value;
+      issue_a(s + 3, st[(j + 3) & 3]);
+      f1.read(st[j], a_rows, b_rows, 1, lane);
+      f0.mma(acc);
+      interleave<F::kReads, L / 2>();
+      wait_vmcnt<L + L / 2>();
+      lds_barrier();
+      issue_b(s + 3, st[(j + 3) & 3]);
+      f0.read(st[(j + 1) & 3], a_rows, b_rows, 0, lane);
+      f1.mma(acc);
+      interleave<F::kReads, L / 2>();
+    };
+    int s = 0;
+    for (; s + 7 <= nk; s += 4) {
+      step(s, std::integral_constant<int, 0>{});
+      step(s + 1, std::integral_constant<int, 1>{});
+      step(s + 2, std::integral_constant<int, 2>{});
+      step(s + 3, std::integral_constant<int, 3>{});
+    }
+    // Last stages: same order with run-time slot selection and counts.
+    for (; s < nk; ++s) {
+      if (s + 3 < nk) issue(s + 3, slot(s + 3));
+      f1.read(slot(s), a_rows, b_rows, 1, lane);
+      f0.mma(acc);
+      if (s + 1 < nk) {
+        const int later = nk - (s + 2) < 2 ? nk - (s + 2) : 2;  // stages issued after s + 1
+        if (later >= 2) wait_vmcnt<2 * L>();
+        else if (later == 1) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        f0.read(slot(s + 1), a_rows, b_rows, 0, lane);
+      }
+      f1.mma(acc);
+    }
+  };
+  constexpr bool kc = AL == KC || BL == KC;
+  if (kc && A.k % BK == 0) kloop(std::false_type{});
+  else kloop(std::integral_constant<bool, kc>{});
   if constexpr (KIND == PLAIN) {
     if (split) {
       // dense 256 x 256 fp32 partial tile (rows and columns past the
@@ -913,86 +921,98 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
     rb[1] = KIND == DX ? DB::kc_rsrc(g.b1, n0) : rb[0];
   }
 
-  // pieces [j0, j1) of this wave's share of A of stage s
-  auto issue_a = [&](int s, char* t, int j0 = 0, int j1 = NT) {
-    if constexpr (KIND == DX) {
-      const bool h = s >= nk1;
-      da.issue_kc(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK2, t, wave, lane, j0, j1);
-    } else if constexpr (AL == KC) {
-      da.issue_kc(ra[0], A.k, s * BK2, t, wave, lane, j0, j1);
-    } else {
-      da.issue_mc(A, m0, A, m0 + 128, s * BK2, t, wave, j0, j1);
-    }
-  };
-  auto issue_b = [&](int s, char* t) {
-    if constexpr (KIND == DX) {
-      const bool h = s >= nk1;
-      const Operand& op = h ? g.b1 : g.b0;
-      if constexpr (BL == KC) db.issue_kc(h ? rb[1] : rb[0], op.k, (h ? s - nk1 : s) * BK2, t, wave, lane);
-      else db.issue_mc(op, n0, op, n0 + 128, (h ? s - nk1 : s) * BK2, t, wave);
-    } else if constexpr (KIND == GATEUP) {
-      if constexpr (BL == KC) db.issue_kc(rb[0], (wave >= 2 ? g.b1 : g.b0).k, s * BK2, t, wave, lane);
-      else db.issue_mc(g.b0, n0, g.b1, n0, s * BK2, t, wave);
-    } else if constexpr (BL == KC) {
-      db.issue_kc(rb[0], B.k, s * BK2, t, wave, lane);
-    } else {
-      db.issue_mc(B, n0, B, n0 + 128, s * BK2, t, wave);
-    }
-  };
-
-  using F = RFrags<E, AL, BL, BK2>;
-  F f0, f1;
-  if (nk > 0) {
-    issue_a(0, R[0]);
-    issue_b(0, R[1]);
-    if (nk > 1) {
-      issue_a(1, R[2]);
-      wait_vmcnt<NT>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();
-    f0.read(R[0], R[1], a_rows, b_rows, 0, lane);
-  }
-  // One stage. `full`: stages s + 1 and s + 2 exist (known at compile time in
-  // the unrolled loop); otherwise the tail checks at run time.
-  // The loads are spread over the sub-steps: B of stage s + 1 (needed first)
-  // over the first, A of stage s + 2 over the second and third.
-  auto stage = [&](int s, char* ca, char* cb, char* na, char* nb, char* na2, bool full) {
-    const bool more = full || s + 1 < nk;
-    const bool more2 = full || s + 2 < nk;
-    if (more) issue_b(s + 1, nb);
-    f1.read(ca, cb, a_rows, b_rows, 1, lane);
-    f0.mma(acc);
-    interleave<F::kReads, NT>();
-    if (more2) issue_a(s + 2, na2, 0, NT / 2);
-    f0.read(ca, cb, a_rows, b_rows, 2, lane);
-    f1.mma(acc);
-    interleave<F::kReads, NT / 2>();
-    if (more2) issue_a(s + 2, na2, NT / 2, NT);
-    f1.read(ca, cb, a_rows, b_rows, 3, lane);
-    f0.mma(acc);
-    interleave<F::kReads, NT / 2>();
-    if (more2) wait_vmcnt<NT>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (more) f0.read(na, nb, a_rows, b_rows, 0, lane);
-    f1.mma(acc);
-    interleave<F::kReads, 0>();
-  };
-  int s = 0;
-  for (; s + 7 <= nk; s += 5) {
-    stage(s + 0, R[0], R[1], R[2], R[3], R[4], true);
-    stage(s + 1, R[2], R[3], R[4], R[0], R[1], true);
-    stage(s + 2, R[4], R[0], R[1], R[2], R[3], true);
-    stage(s + 3, R[1], R[2], R[3], R[4], R[0], true);
-    stage(s + 4, R[3], R[4], R[0], R[1], R[2], true);
-  }
   auto reg = [&](int t) -> char* {
     t %= 5;
     return t == 0 ? R[0] : t == 1 ? R[1] : t == 2 ? R[2] : t == 3 ? R[3] : R[4];
   };
-  for (; s < nk; ++s) stage(s, reg(2 * s), reg(2 * s + 1), reg(2 * s + 2), reg(2 * s + 3), reg(2 * s + 4), false);
+  // The K loop, compiled with (KT) and without the K-tail checks of K-major
+  // loads; the epilogue after it exists once.
+  auto kloop = [&](auto KTc) {
+    constexpr bool KT = decltype(KTc)::value;
+    // pieces [j0, j1) of this wave's share of A of stage s
+    auto issue_a = [&](int s, char* t, int j0 = 0, int j1 = NT) {
+      if constexpr (KIND == DX) {
+        const bool h = s >= nk1;
+        da.template issue_kcr<KT>(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK2, t, wave, lane, j0, j1);
+      } else if constexpr (AL == KC) {
+        da.template issue_kcr<KT>(ra[0], A.k, s * BK2, t, wave, lane, j0, j1);
+      } else {
+        da.issue_mc(A, m0, A, m0 + 128, s * BK2, t, wave, j0, j1);
+      }
+    };
+    auto issue_b = [&](int s, char* t) {
+      if constexpr (KIND == DX) {
+        const bool h = s >= nk1;
+        const Operand& op = h ? g.b1 : g.b0;
+        if constexpr (BL == KC) db.template issue_kcr<KT>(h ? rb[1] : rb[0], op.k, (h ? s - nk1 : s) * BK2, t, wave, lane);
+        else db.issue_mc(op, n0, op, n0 + 128, (h ? s - nk1 : s) * BK2, t, wave);
+      } else if constexpr (KIND == GATEUP) {
+        if constexpr (BL == KC) db.template issue_kcr<KT>(rb[0], (wave >= 2 ? g.b1 : g.b0).k, s * BK2, t, wave, lane);
+        else db.issue_mc(g.b0, n0, g.b1, n0, s * BK2, t, wave);
+      } else if constexpr (BL == KC) {
+        db.template issue_kcr<KT>(rb[0], B.k, s * BK2, t, wave, lane);
+      } else {
+        db.issue_mc(B, n0, B, n0 + 128, s * BK2, t, wave);
+      }
+    };
+
+    using F = RFrags<E, AL, BL, BK2>;
+    F f0, f1;
+    if (nk > 0) {
+      issue_a(0, R[0]);
+      issue_b(0, R[1]);
+      if (nk > 1) {
+        issue_a(1, R[2]);
+        wait_vmcnt<NT>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      f0.read(R[0], R[1], a_rows, b_rows, 0, lane);
+    }
+    // One stage. `full`: stages s + 1 and s + 2 exist (known at compile time in
+    // the unrolled loop); otherwise the tail checks at run time.
+    // The loads are spread over the sub-steps: B of stage s + 1 (needed first)
+    // over the first, A of stage s + 2 over the second and third.
+    auto stage = [&](int s, char* ca, char* cb, char* na, char* nb, char* na2, bool full) {
+      const bool more = full || s + 1 < nk;
+      const bool more2 = full || s + 2 < nk;
+      // stages scheduled one at a time: without this fence the scheduler
+      // gathered up to 14 loads of neighbouring stages into one burst
+      // (dA + dSwiGLU 4 % slower); dI measured no better with it
+      if constexpr (KIND != DX) __builtin_amdgcn_sched_barrier(0);
+      if (more) issue_b(s + 1, nb);
+      f1.read(ca, cb, a_rows, b_rows, 1, lane);
+      f0.mma(acc);
+      interleave<F::kReads, NT>();
+      if (more2) issue_a(s + 2, na2, 0, NT / 2);
+      f0.read(ca, cb, a_rows, b_rows, 2, lane);
+      f1.mma(acc);
+      interleave<F::kReads, NT / 2>();
+      if (more2) issue_a(s + 2, na2, NT / 2, NT);
+      f1.read(ca, cb, a_rows, b_rows, 3, lane);
+      f0.mma(acc);
+      interleave<F::kReads, NT / 2>();
+      if (more2) wait_vmcnt<NT>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (more) f0.read(na, nb, a_rows, b_rows, 0, lane);
+      f1.mma(acc);
+      interleave<F::kReads, 0>();
+    };
+    int s = 0;
+    for (; s + 7 <= nk; s += 5) {
+      stage(s + 0, R[0], R[1], R[2], R[3], R[4], true);
+      stage(s + 1, R[2], R[3], R[4], R[0], R[1], true);
+      stage(s + 2, R[4], R[0], R[1], R[2], R[3], true);
+      stage(s + 3, R[1], R[2], R[3], R[4], R[0], true);
+      stage(s + 4, R[3], R[4], R[0], R[1], R[2], true);
+    }
+    for (; s < nk; ++s) stage(s, reg(2 * s), reg(2 * s + 1), reg(2 * s + 2), reg(2 * s + 3), reg(2 * s + 4), false);
+  };
+  constexpr bool kc = AL == KC || BL == KC;
+  if (kc && A.k % BK2 == 0) kloop(std::false_type{});
+  else kloop(std::integral_constant<bool, kc>{});
   // (a select, not R[wave]: indexing R at run time would keep it in scratch)
   ring_epilogue<E, KIND>(g, C, acc, m0, n0, wm, wn, lane, reg(wave));
 }
