@@ -1774,11 +1774,12 @@ static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
 // Tile walk of the ring kernels (tile_coords): each XCD runs group_m M-tiles
 // x (32 / group_m) N-tiles at a time, so that its concurrent tiles share
 // operand rows through its L2. Per stage, measured over 2, 4 and 8 at
-// D = 4096, H = 11008, T = 65536 (the differences are 0.5-2.5 %): 2 for
-// gate/up, down and dI; 4 for the weight gradients; 8 for dA + dSwiGLU.
+// D = 4096, H = 11008, T = 65536 (the differences are 0.5-3 %): 2 for
+// gate/up, 8 for dA + dSwiGLU, 4 for the others (down, dI and the weight
+// gradients).
 template <int KIND, int STAGE>
 constexpr int ring_group_m() {
-  return KIND == DSWIGLU ? 8 : (STAGE == 3 || STAGE == 4) ? 4 : 2;
+  return KIND == DSWIGLU ? 8 : KIND == GATEUP ? 2 : 4;
 }
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
