@@ -385,6 +385,86 @@ def infer_sweep(mlp, torch, dev, reps=20, copy_gbps=None):
     return out
 
 
+def vendor_gemm(torch, dev, reps=10):
+    """Context, not part of the step: hipBLASLt (torch.mm) on two of the
+    step's GEMM shapes at D=4096, H=11008, T=65536, without the fused
+    epilogues. dI's shape with both operands K-major ([T, 2H] times a
+    transposed [D, 2H]), and gate/up's with X K-major and [Wg | Wu] N-major.
+    Timed with events on torch's stream after two warm-up calls."""
+    T, D, H = 65536, 4096, 11008
+    bf = torch.bfloat16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    out = {}
+
+    def run(name, a, b):
+        for _ in range(2):
+            c = torch.mm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        del c
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * a.shape[0] * a.shape[1] * b.shape[1] / ms / 1e9
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    dg = torch.randn(T, 2 * H, device=dev, dtype=bf, generator=gen)
+    w = torch.randn(D, 2 * H, device=dev, dtype=bf, generator=gen)
+    run("dI_shape_KxK", dg, w.t())
+    del dg, w
+    x = torch.randn(T, D, device=dev, dtype=bf, generator=gen)
+    wgu = torch.randn(D, 2 * H, device=dev, dtype=bf, generator=gen)
+    run("gateup_shape_KxN", x, wgu)
+    return out
+
+
+def ingest_vendor(pass_a_csv, out_md, command):
+    """Clock and matrix-core occupancy of the hipBLASLt kernels of
+    `bench.py --vendor-gemm` from one counter pass (the same counters and
+    formulas as ingest_counters). The GEMM kernels (names containing "Cijk")
+    are told apart by order of first appearance: dI's shape, then
+    gate/up's. Means over the last 4 dispatches of each."""
+    import csv
+    from collections import OrderedDict, defaultdict
+
+    per = OrderedDict()
+    with open(pass_a_csv) as f:
+        for r in csv.DictReader(f):
+            n = r["Kernel_Name"]
+            if "Cijk" not in n:
+                continue
+            d = per.setdefault(n, defaultdict(dict))[r["Dispatch_Id"]]
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["dur_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    labels = ["dI shape, both K-major", "gate/up shape, X K-major, W N-major"]
+    lines = ["| GEMM | kernel | ms | sclk GHz | MFMA busy % | effective % of peak | wait % |",
+             "|---|---|---|---|---|---|---|"]
+    for label, (name, disp) in zip(labels, per.items()):
+        rows = [disp[k] for k in sorted(disp, key=int)][-4:]
+        ms = sum(r["dur_ns"] for r in rows) / len(rows) / 1e6
+        cyc = sum(r["GRBM_GUI_ACTIVE"] for r in rows) / len(rows) / 8
+        sclk = cyc / (ms * 1e-3) / 1e9
+        busy = sum(r["SQ_VALU_MFMA_BUSY_CYCLES"] for r in rows) / len(rows) / (cyc * 1024)
+        wait = sum(r["SQ_WAIT_ANY"] for r in rows) / max(sum(r["SQ_WAVE_CYCLES"] for r in rows), 1)
+        short = name if len(name) <= 60 else name[:57] + "..."
+        lines.append(f"| {label} | `{short}` | {ms:.3f} | {sclk:.2f} | {100 * busy:.1f} | "
+                     f"{100 * sclk * busy / 2.4:.1f} | {100 * wait:.1f} |")
+    head = ("# hipBLASLt at two of the step's GEMM shapes (context): clock and matrix-core occupancy, bf16\n\n"
+            "D=4096, H=11008, T=65536, plain GEMMs through torch.mm, no fused epilogue. Commands (repository "
+            f"root, one MI355X):\n\n```\n{command}\n```\n\n"
+            "ms: duration of each dispatch in the counter run (kernels run one at a time there). sclk: "
+            "GRBM_GUI_ACTIVE / 8 over the duration. MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (per-XCD cycles x "
+            "1024 SIMDs). Effective % of peak: sclk x busy / 2.4 GHz. Wait %: SQ_WAIT_ANY / SQ_WAVE_CYCLES. "
+            "The same counters for this repository's kernels are in counters_swiglu_fwd_bwd_T65536_bf16.md.\n\n")
+    with open(out_md, "w") as f:
+        f.write(head + "\n".join(lines) + "\n")
+    print(head + "\n".join(lines))
+
+
 def fp32_leg(mlp, torch, dev, steps=10, warmup=3):
     """True-IEEE fp32 mode at D=2048, H=5632, B=8, S=512 (T=4096): mean step time
     of fwd + bwd and TFLOP/s (18*T*D*H) against the fp32 matrix peak."""
@@ -816,6 +896,9 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--ingest-infer":
         ingest_infer(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], " ".join(sys.argv[6:]))
         return
+    if len(sys.argv) > 1 and sys.argv[1] == "--ingest-vendor":
+        ingest_vendor(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -831,6 +914,8 @@ def main():
     ap.add_argument("--no-tp", action="store_true", help="skip the tensor-parallel shard-shape sweep")
     ap.add_argument("--no-linear", action="store_true", help="skip the nn.Linear weight-layout leg")
     ap.add_argument("--no-clock", action="store_true", help="skip the 3 s graphics-clock window (profiled runs)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only hipBLASLt (torch.mm) at two of the step's GEMM shapes, for context: one JSON line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known traffic, used to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -849,6 +934,9 @@ def main():
     if args.infer_trace:
         order = infer_trace(mlp, torch, torch.device("cuda:0"))
         print(json.dumps({"infer_trace": order, "calls_per_shape": INFER_TRACE_CALLS}), flush=True)
+        return
+    if args.vendor_gemm:
+        print(json.dumps({"vendor_gemm": vendor_gemm(torch, torch.device("cuda:0"))}), flush=True)
         return
     if args.infer_only:
         dev = torch.device("cuda:0")
