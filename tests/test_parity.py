@@ -117,6 +117,13 @@ def test_fp32_and_fp16_ragged(mlp):
         _check_full(mlp, inp, fmt, f"{fmt} T=333 D=136 H=264")
 
 
+def test_fp16_ragged_ring(mlp):
+    # T > 512 takes the ring kernels; D and H leave a K tail in every stage
+    # (136, 200 = 8 mod 32 and mod 64)
+    inp = make_inputs(777, 136, 200, seed=77, dtype="fp16")
+    _check_full(mlp, inp, "fp16", "fp16 T=777 D=136 H=200")
+
+
 def _one_per_block(n, rng, b=32):
     """One index in every b-wide block of range(n) (the last block may be
     partial), drawn at random within the block."""
