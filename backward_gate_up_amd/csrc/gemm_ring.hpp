@@ -14,8 +14,14 @@
 //     row r sits at chunk c ^ ((r >> 2) & 3), so the 16 rows that one
 //     16-lane group of a ds_read_b128 reads fall on 16 distinct bank quads.
 //   M/N-major (MC) tile: two 128-column sub-tiles of 32 K rows x 256 B; chunk
-//     c (0..15) of K row kr sits at c ^ ((kr & 3) << 2), so the 4 K rows x 4
-//     chunks that 32 lanes of a ds_read_b64_tr_b16 read are distinct.
+//     c (0..15) of K row kr sits at c ^ mc_swz(kr), so the two 16-lane
+//     groups of a half-wave of ds_read_b64_tr_b16 (4 K rows each, 8 rows
+//     apart, 32 bytes per row) read 8 distinct 32-byte bank ranges.
+//
+// The matrix cores run v_mfma_f32_16x16x32: measured on all CUs under the
+// chip's power limit, back-to-back 16x16x32 MFMAs sustain 2041 TFLOP/s
+// against 1780 for 32x32x16 (the wider instruction reads and writes a
+// 16-register accumulator per 16 K, the narrower 4 registers per 32 K).
 // One buffer_load_dwordx4 ... lds writes 1 KiB of consecutive LDS (lane i at
 // M0 + 16 i, measured on the device), so the swizzle is applied on the global
 // side: each lane fetches the logical chunk that belongs at its slot.
@@ -66,10 +72,13 @@ __device__ __forceinline__ int kc_off(int r, int c) {
   return r * Geo<BKT>::ROWB + ((c ^ kc_swz<BKT>(r)) << 4);
 }
 
+// MC chunk swizzle of K row kr: bits 2-3 from kr & 3, bit 1 from kr & 8.
+__device__ __forceinline__ int mc_swz(int kr) { return ((kr & 3) << 2) | (((kr >> 3) & 1) << 1); }
+
 template <int BKT>
 __device__ __forceinline__ int mc_off(int kr, int col) {
   const int sub = col >> 7, cc = col & 127;
-  return sub * Geo<BKT>::SUB + kr * 256 + (((cc >> 3) ^ ((kr & 3) << 2)) << 4) + (cc & 7) * 2;
+  return sub * Geo<BKT>::SUB + kr * 256 + (((cc >> 3) ^ mc_swz(kr)) << 4) + (cc & 7) * 2;
 }
 
 template <int N>
@@ -104,7 +113,7 @@ struct Dma {
         voff[j] = (r0 + rr < op.rows) ? (uint32_t)(rr * (int)op.ld * 2 + c * 16) : kOOB;
       } else {
         const int kr = ((wave & 1) * G::PPW + j) * 4 + (lane >> 4);
-        const int c = (lane & 15) ^ ((kr & 3) << 2);
+        const int c = (lane & 15) ^ mc_swz(kr);
         voff[j] = (uint32_t)(kr * (int)op.ld * 2 + c * 16);
       }
     }
@@ -202,17 +211,21 @@ struct Dma {
   }
 };
 
-// Operand fragment (8 consecutive K of row ro + (lane & 31), K = ks*16 +
-// (lane >> 5)*8 + 0..7) from a ring stage tile.
+// Operand fragment of v_mfma_f32_16x16x32: 8 consecutive K of row (KC) or
+// column (MC) ro + (lane & 15), K = ks * 32 + (lane >> 4) * 8 + 0..7, from a
+// ring stage tile.
 template <int LAYOUT, int BKT = BK>
 __device__ __forceinline__ u32x4_t frag(const char* tile, int ro, int ks, int lane) {
   if constexpr (LAYOUT == KC) {
-    return *(const u32x4_t*)(tile + kc_off<BKT>(ro + (lane & 31), ks * 2 + (lane >> 5)));
+    return *(const u32x4_t*)(tile + kc_off<BKT>(ro + (lane & 15), ks * 4 + (lane >> 4)));
   } else {
-    // ds_read_b64_tr_b16 (lane i of each 16-lane block receives element j
-    // from the address of lane 4j + i/4, column i % 4)
-    const int krow = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
-    const int col = ro + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    // ds_read_b64_tr_b16: lane i of each 16-lane block receives element j
+    // from the address of lane 4j + i/4, column i % 4. Lane r of block b
+    // points at K row ks*32 + 8b + r/4 (and + 4), columns ro + 4 (r % 4)
+    // .. + 3, so after the transpose lane i of block b holds column ro + i,
+    // K rows ks*32 + 8b .. + 7.
+    const int krow = ks * 32 + (lane >> 4) * 8 + ((lane & 15) >> 2);
+    const int col = ro + (lane & 3) * 4;
     s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off<BKT>(krow, col)));
     s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off<BKT>(krow + 4, col)));
     u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
@@ -220,46 +233,119 @@ __device__ __forceinline__ u32x4_t frag(const char* tile, int ro, int ks, int la
   }
 }
 
+// One wave's fragments for the 32-K steps of its 128 x 128 block, in four
+// groups of four: A rows 0-63 and 64-127 (a[0], a[1]) and B columns 0-63 and
+// 64-127 (b[0], b[1]), 64 registers. A step runs four quadrants of 16 MFMAs,
+// one A half times one B half each, in an order that alternates with the
+// step's parity P (f = P, s = 1 - P):
+//   Q0 = a[0] x b[f], Q1 = a[0] x b[s], Q2 = a[1] x b[s], Q3 = a[1] x b[f].
+// a[0] is last used in Q1, b[s] in Q2, a[1] and b[f] in Q3, and the next
+// step (parity 1 - P) starts with a[0] x b[s]. So each quadrant reads one
+// group into registers freed by the quadrant before and needed by the
+// quadrant after: Q0 reads b[s] of this step, Q1 a[1] of this step, Q2 a[0]
+// of the next, Q3 b[s] of the next (its b[f']). With the new group's
+// fragments in the outer loop of the quadrant that uses it, every LDS read
+// has at least 16 MFMAs to land, and no group is double-buffered.
+//
+// The MFMAs are volatile statements, and the compiler keeps loads and LDS
+// reads in their source order around them, so the interleave written here
+// is the one issued: fragment k of a quadrant's group is read after its
+// MFMA k, and its NL global loads follow MFMAs 1, 1 + 16/NL, ... (all four
+// waves leave a barrier together; loads issued back to back would queue at
+// the texture unit at once and hold up the MFMA issue behind them).
 template <class E, int AL, int BL, int BKT = BK>
-struct RFrags {
-  u32x4_t a[4], b[4];
-  // A tile at `at`, B tile at `bt`
-  __device__ __forceinline__ void read(const char* at, const char* bt, const int (&ar)[4], const int (&br)[4],
-                                       int ks, int lane) {
+struct RingFrags {
+  u32x4_t a[2][4], b[2][4];
+
+  template <int H>
+  __device__ __forceinline__ void read_a(const char* at, const int (&ar)[8], int ks, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = frag<BL, BKT>(bt, br[j], ks, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = frag<AL, BKT>(at, ar[i], ks, lane);
+    for (int k = 0; k < 4; ++k) a[H][k] = frag<AL, BKT>(at, ar[4 * H + k], ks, lane);
   }
-  __device__ __forceinline__ void read(const char* stage, const int (&ar)[4], const int (&br)[4], int ks,
-                                       int lane) {
-    read(stage, stage + Geo<BKT>::OPB, ar, br, ks, lane);
-  }
-  __device__ __forceinline__ void mma(f32x16_t (&acc)[4][4]) const {
+  template <int H>
+  __device__ __forceinline__ void read_b(const char* bt, const int (&br)[8], int ks, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = E::mfma(b[j], a[i], acc[i][j]);
+    for (int k = 0; k < 4; ++k) b[H][k] = frag<BL, BKT>(bt, br[4 * H + k], ks, lane);
   }
-  static constexpr int kReads = 4 * (AL == MC ? 2 : 1) + 4 * (BL == MC ? 2 : 1);
+  // acc[4 HA + i][4 HB + j] += A x B (acc[i][j], lane l: output row
+  // ar[i] + l % 16, columns br[j] + (l / 16) * 4 .. + 3); after(n) runs
+  // after MFMA n (a constant once unrolled). BN: B fragments in the outer
+  // loop (n = 4 j + i), for a quadrant whose B group was read in the
+  // quadrant before: fragment k is then first used by MFMA 4 k, not k.
+  template <int HA, int HB, bool BN, class After>
+  __device__ __forceinline__ void quad(f32x4_t (&acc)[8][8], After&& after) {
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int i = BN ? p : o, j = BN ? o : p;
+        E::mfma16(acc[4 * HA + i][4 * HB + j], b[HB][j], a[HA][i]);
+        after(4 * o + p);
+      }
+  }
+
+  // One step of parity P on the stage tile (at, bt) at K offset ks * 32.
+  // mid() runs between Q1 and Q2 (the barrier that publishes the next
+  // step's tile, if that is a new stage); the next step's fragments come
+  // from (nat, nbt, nks) when NX. issue(q, k) issues load k (< NL) of
+  // quadrant q.
+  template <int P, int NL, bool NX, class Mid, class Issue>
+  __device__ __forceinline__ void step(f32x4_t (&acc)[8][8], const char* at, const char* bt, int ks,
+                                       const char* nat, const char* nbt, int nks, const int (&ar)[8],
+                                       const int (&br)[8], int lane, Mid&& mid, Issue&& issue) {
+    constexpr int F = P, S = 1 - P;
+    static_assert(NL > 0 && NL <= 16 && 16 % NL == 0, "loads per quadrant");
+    constexpr int EV = 16 / NL;
+    auto load = [&](int q, int n) {
+      if (n % EV == 1) issue(q, n / EV);
+    };
+    // Q0 and Q1 take the B group read in the quadrant before, Q2 the A
+    // group; Q3 has none new
+    quad<0, F, true>(acc, [&](int n) {
+      if (n < 4) b[S][n] = frag<BL, BKT>(bt, br[4 * S + n], ks, lane);
+      load(0, n);
+    });
+    quad<0, S, true>(acc, [&](int n) {
+      if (n < 4) a[1][n] = frag<AL, BKT>(at, ar[4 + n], ks, lane);
+      load(1, n);
+    });
+    mid();
+    quad<1, S, false>(acc, [&](int n) {
+      if (NX && n < 4) a[0][n] = frag<AL, BKT>(nat, ar[n], nks, lane);
+      load(2, n);
+    });
+    quad<1, F, false>(acc, [&](int n) {
+      if (NX && n < 4) b[S][n] = frag<BL, BKT>(nbt, br[4 * S + n], nks, lane);
+      load(3, n);
+    });
+  }
 };
 
-// Scheduling hint for one sub-step of 16 MFMAs: each MFMA is followed by its
-// share of the next sub-step's LDS reads, and the NVM loads are spaced evenly
-// (one after every 16/NVM-th MFMA). All four waves reach this point together
-// after a barrier; issuing a stage's loads back to back would queue 4 x 8
-// loads at the texture unit at once and stall the MFMA issue behind them.
-template <int NDS, int NVM>
-__device__ __forceinline__ void interleave() {
-  constexpr int pd = (NDS + 15) / 16;
-  static_assert(NVM == 0 || (NVM <= 16 && 16 % NVM == 0), "loads per sub-step");
-  constexpr int every = NVM > 0 ? 16 / NVM : 0;
+// The compiler does not see the MFMAs above as MFMAs, so it inserts none of
+// the wait states that separate an MFMA from VALU work on its registers.
+// acc_fence is a row of empty volatile statements, one per accumulator row,
+// that each take the row as an in-out operand, so VALU accesses of a row
+// stay on their side of its statement and the statements keep their order.
+// START (after the zero fill): the last statement waits 5 states, which
+// every fill precedes and every MFMA follows (a VALU result read by an
+// MFMA). End (before the epilogue): the first one waits 24 states, which
+// every MFMA precedes and every VALU read of an accumulator follows.
+template <bool START>
+__device__ __forceinline__ void acc_fence(f32x4_t (&acc)[8][8]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, pd, 0);
-    if constexpr (NVM > 0)
-      if (i % every == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  for (int i = 0; i < 8; ++i) {
+    if (START ? i == 7 : i == 0) {
+      if constexpr (START)
+        asm volatile("s_nop 4" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
+                     "+a"(acc[i][4]), "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+      else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    } else {
+      asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                   "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    }
   }
 }
 

@@ -60,6 +60,18 @@ struct Bf16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, p),
                                                    __builtin_bit_cast(bf16x8_t, q), c, 0, 0, 0);
   }
+  // 16 x 16 x 32: lane l holds row l % 16 of p and column l % 16 of q, K
+  // (l / 16) * 8 .. + 7; the result's lane l holds column l % 16, rows
+  // (l / 16) * 4 .. + 3
+  // c += p x q in place: the accumulator stays in its AGPRs (the builtin's
+  // 4-register results are not kept tied to their inputs by the register
+  // allocator, which then copies and spills them). A volatile statement also
+  // keeps its place among the loads, so the source order is the issue order.
+  // The compiler inserts no MFMA hazard waits around it: callers separate the
+  // first and last MFMA of a tile from VALU accesses of the accumulators.
+  static __device__ __forceinline__ void mfma16(f32x4_t& c, u32x4_t p, u32x4_t q) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(p), "v"(q));
+  }
   static __device__ __forceinline__ elem from_f32(float x) { return (__bf16)x; }
   static __device__ __forceinline__ float to_f32(elem x) { return (float)x; }
 };
@@ -72,6 +84,9 @@ struct Fp16 {
   static __device__ __forceinline__ f32x16_t mfma(u32x4_t p, u32x4_t q, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, p),
                                                   __builtin_bit_cast(f16x8_t, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void mfma16(f32x4_t& c, u32x4_t p, u32x4_t q) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(p), "v"(q));
   }
   static __device__ __forceinline__ elem from_f32(float x) { return (_Float16)x; }
   static __device__ __forceinline__ float to_f32(elem x) { return (float)x; }

@@ -523,38 +523,38 @@ struct WaveBlock {
 };
 
 template <class E, int KIND>
-__device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t (&acc)[4][4], int m0, int n0,
+__device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x4_t (&acc)[8][8], int m0, int n0,
                                               int wm, int wn, int lane, char* wbuf) {
   using V4 = typename E::vec4;
-  const int ml = lane & 31;
-  const int nl = (lane >> 5) * 4;
+  // acc[i][j] holds this wave's row 16 i + ml, columns 16 j + nl .. + 3
+  const int ml = lane & 15;
+  const int nl = (lane >> 4) * 4;
   ring::lds_barrier();  // every wave is done reading the K-loop stages
   if constexpr (KIND == GATEUP) {
     // wave block: 128 rows (t) x 64 hidden units, planes A, G, U
     WaveBlock<E, 64> pa{wbuf}, pg{wbuf + 16384};
     const int r0 = m0 + wm * 128, c0 = n0 + wn * 64;
     // A and G into LDS; the program (one- or two-round) is fixed per launch
+    // (column blocks 0-3 of the wave are G, 4-7 the matching U)
     auto stage_ag = [&](auto two) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j) {
+          V4 gv, av;
+          float gf[4], uf[4], sg[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            V4 gv, av;
-            float gf[4], uf[4], sg[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              gv[e] = E::from_f32(acc[i][j][q * 4 + e]);
-              gf[e] = E::to_f32(gv[e]);
-              uf[e] = E::to_f32(E::from_f32(acc[i][j + 2][q * 4 + e]));
-            }
-            sigmoid4<E>(gf, sg);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) av[e] = swiglu_a_s<E, decltype(two)::value>(gf[e], sg[e], uf[e]);
-            pa.put4(i * 32 + ml, j * 32 + q * 8 + nl, av);
-            pg.put4(i * 32 + ml, j * 32 + q * 8 + nl, gv);
+          for (int e = 0; e < 4; ++e) {
+            gv[e] = E::from_f32(acc[i][j][e]);
+            gf[e] = E::to_f32(gv[e]);
+            uf[e] = E::to_f32(E::from_f32(acc[i][j + 4][e]));
           }
+          sigmoid4<E>(gf, sg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[e] = swiglu_a_s<E, decltype(two)::value>(gf[e], sg[e], uf[e]);
+          pa.put4(i * 16 + ml, j * 16 + nl, av);
+          pg.put4(i * 16 + ml, j * 16 + nl, gv);
+        }
     };
     if (g.two_round) stage_ag(std::true_type{});
     else stage_ag(std::false_type{});
@@ -563,21 +563,19 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
       pg.template store<128>(g.c1, g.ldc, r0, c0, g.M, g.N, lane);
       WaveBlock<E, 64> pu{wbuf};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j) {
+          V4 uv;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            V4 uv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) uv[e] = E::from_f32(acc[i][j + 2][q * 4 + e]);
-            pu.put4(i * 32 + ml, j * 32 + q * 8 + nl, uv);
-          }
+          for (int e = 0; e < 4; ++e) uv[e] = E::from_f32(acc[i][j + 4][e]);
+          pu.put4(i * 16 + ml, j * 16 + nl, uv);
+        }
       pu.template store<128>(g.c2, g.ldc, r0, c0, g.M, g.N, lane);
     }
   } else if constexpr (KIND == DSWIGLU) {
     // wave block: 128 rows x 128 hidden units, in four quarters of 32 rows
-    // (one MFMA row block each). The G and U rows of a quarter are loaded
+    // (two MFMA row blocks each). The G and U rows of a quarter are loaded
     // into LDS, turned into dG and dU in place (this tile's own (t, h) block
     // only) and stored back. Two LDS slots of 16 KiB: the loads of quarter
     // q + 1 are in flight while quarter q is computed and stored, and those
@@ -606,26 +604,26 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
       WaveBlock<E, 128> pg{wbuf + (q & 1) * 16384}, pu{wbuf + (q & 1) * 16384 + 8192};
       // every G and U value of the quarter first (one LDS latency), then
       // the math
-      V4 gv[4][4], uv[4][4];
+      V4 gv[2][8], uv[2][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          gv[j][qq] = pg.get4(ml, j * 32 + qq * 8 + nl);
-          uv[j][qq] = pu.get4(ml, j * 32 + qq * 8 + nl);
+        for (int j = 0; j < 8; ++j) {
+          gv[h][j] = pg.get4(h * 16 + ml, j * 16 + nl);
+          uv[h][j] = pu.get4(h * 16 + ml, j * 16 + nl);
         }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int r = ml, c = j * 32 + qq * 8 + nl;
+        for (int j = 0; j < 8; ++j) {
+          const int r = h * 16 + ml, c = j * 16 + nl;
           V4 dg, du;
           float da[4], gf[4], uf[4], dgf[4], duf[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            da[e] = acc[q][j][qq * 4 + e];
-            gf[e] = E::to_f32(gv[j][qq][e]);
-            uf[e] = E::to_f32(uv[j][qq][e]);
+            da[e] = acc[2 * q + h][j][e];
+            gf[e] = E::to_f32(gv[h][j][e]);
+            uf[e] = E::to_f32(uv[h][j][e]);
           }
           dswiglu4<E>(da, gf, uf, dgf, duf);
 #pragma unroll
@@ -650,16 +648,14 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
     // PLAIN / DX: 128 x 128 block of C
     WaveBlock<E, 128> pc{wbuf};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j) {
+        V4 v;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          V4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = E::from_f32(acc[i][j][q * 4 + e]);
-          pc.put4(i * 32 + ml, j * 32 + q * 8 + nl, v);
-        }
+        for (int e = 0; e < 4; ++e) v[e] = E::from_f32(acc[i][j][e]);
+        pc.put4(i * 16 + ml, j * 16 + nl, v);
+      }
     pc.template store<128>(C, g.ldc, m0 + wm * 128, n0 + wn * 128, g.M, g.N, lane);
   }
 }
@@ -667,6 +663,19 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x16_t 
 // One 256 x 256 output tile on the direct-to-LDS ring (16-bit types; see
 // gemm_ring.hpp). st0..st3 are the four stage arrays; separate arrays let the
 // compiler wait for exactly the stage a read needs.
+// A piece of a split weight-gradient tile: the dense 256 x 256 fp32 partial
+// tile `piece` (rows and columns past the matrix hold sums of zero operands;
+// the reduction skips them); each lane holds 4 consecutive columns.
+__device__ __forceinline__ void ring_partial_store(const KArgs& g, const f32x4_t (&acc)[8][8], int piece,
+                                                   const int (&a_rows)[8], const int (&b_rows)[8], int lane) {
+  float* P = g.P + (int64_t)piece * 65536;
+  const int ml = lane & 15, nl = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *(f32x4_t*)(P + (a_rows[i] + ml) * 256 + b_rows[j] + nl) = acc[i][j];
+}
+
 template <class E, int AL, int BL, int KIND>
 __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, char* st2, char* st3, int bid,
                                           int bz, int ks = 0, int piece = -1) {
@@ -688,18 +697,25 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
     else B = g.b1;
     C = g.c1;
   }
-  int a_rows[4], b_rows[4];
+  // this wave's 16-row blocks of A and 16-column blocks of B (gate/up:
+  // four of Wg, then the same four of Wu)
+  int a_rows[8], b_rows[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_rows[i] = wm * 128 + i * 32;
+  for (int i = 0; i < 8; ++i) a_rows[i] = wm * 128 + i * 16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    b_rows[j] = (KIND == GATEUP) ? (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+  for (int j = 0; j < 8; ++j)
+    b_rows[j] = (KIND == GATEUP) ? (j < 4 ? 0 : 128) + wn * 64 + (j & 3) * 16 : wn * 128 + j * 16;
 
-  f32x16_t acc[4][4];
+  // zeroed inside the K loop, after its prologue: the fence makes the zeros
+  // opaque, and live across the prologue they were spilled, not rebuilt
+  f32x4_t acc[8][8];
+  auto zero_acc = [&] {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{};
+    acc_fence<true>(acc);
+  };
 
   Dma<AL> da;
   Dma<BL> db;
@@ -749,109 +765,121 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
   // loads; the epilogue after it exists once.
   auto kloop = [&](auto KTc) {
     constexpr bool KT = decltype(KTc)::value;
-    auto issue_a = [&](int s, char* stg) {
+    constexpr int PW = Geo<BK>::PPW;  // loads per wave per operand tile
+    // this wave's loads [j0, j1) of A / B of stage s into stage array stg
+    auto issue_a = [&](int s, char* stg, int j0, int j1) {
       if constexpr (KIND == DX) {
         const bool h = s >= nk1;
-        da.template issue_kcr<KT>(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK, stg, wave, lane);
+        da.template issue_kcr<KT>(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK, stg, wave, lane,
+                                  j0, j1);
       } else if constexpr (AL == KC) {
-        da.template issue_kcr<KT>(ra[0], A.k, (sb + s) * BK, stg, wave, lane);
+        da.template issue_kcr<KT>(ra[0], A.k, (sb + s) * BK, stg, wave, lane, j0, j1);
       } else {
-        da.issue_mcs(ma[0], (sb + s) * BK, stg, wave);
+        da.issue_mcs(ma[0], (sb + s) * BK, stg, wave, j0, j1);
       }
     };
-    auto issue_b = [&](int s, char* stg) {
+    auto issue_b = [&](int s, char* stg, int j0, int j1) {
       if constexpr (KIND == DX) {
         const bool h = s >= nk1;
         if constexpr (BL == KC)
-          db.template issue_kcr<KT>(h ? rb[1] : rb[0], h ? g.b1.k : g.b0.k, (h ? s - nk1 : s) * BK, stg + OPB, wave, lane);
-        else db.issue_mcs(h ? mb[1] : mb[0], (h ? s - nk1 : s) * BK, stg + OPB, wave);
+          db.template issue_kcr<KT>(h ? rb[1] : rb[0], h ? g.b1.k : g.b0.k, (h ? s - nk1 : s) * BK, stg + OPB, wave,
+                                    lane, j0, j1);
+        else db.issue_mcs(h ? mb[1] : mb[0], (h ? s - nk1 : s) * BK, stg + OPB, wave, j0, j1);
       } else if constexpr (BL == KC) {
-        db.template issue_kcr<KT>(rb[0], KIND == GATEUP ? (wave >= 2 ? g.b1.k : g.b0.k) : B.k, (sb + s) * BK, stg + OPB, wave,
-                    lane);
+        db.template issue_kcr<KT>(rb[0], KIND == GATEUP ? (wave >= 2 ? g.b1.k : g.b0.k) : B.k, (sb + s) * BK,
+                                  stg + OPB, wave, lane, j0, j1);
       } else {
-        db.issue_mcs(mb[0], (sb + s) * BK, stg + OPB, wave);
+        db.issue_mcs(mb[0], (sb + s) * BK, stg + OPB, wave, j0, j1);
       }
     };
     auto issue = [&](int s, char* stg) {
-      issue_a(s, stg);
-      issue_b(s, stg);
+      issue_a(s, stg, 0, PW);
+      issue_b(s, stg, 0, PW);
     };
-
-    using F = RFrags<E, AL, BL>;
-    F f0, f1;
+    using F = RingFrags<E, AL, BL>;
+    F fr;
+    // Stage s is one step. Its fragments are read from Q2 of stage s - 1 to
+    // Q1 of stage s; between Q1 and Q2 this wave's loads of stage s + 1 have
+    // landed (those of s + 2 and s + 3 may be in flight) and a barrier
+    // publishes every wave's. Every wave is then done with stage s's slot,
+    // so Q2 and Q3 issue the loads of stage s + 4 into it.
     if (nk > 0) {
       issue(0, st0);
       if (nk > 1) issue(1, st1);
       if (nk > 2) issue(2, st2);
-      if (nk > 2) wait_vmcnt<2 * L>();
+      if (nk > 3) issue(3, st3);
+      if (nk > 3) wait_vmcnt<3 * L>();
+      else if (nk > 2) wait_vmcnt<2 * L>();
       else if (nk > 1) wait_vmcnt<L>();
       else wait_vmcnt<0>();
       lds_barrier();
-      f0.read(st0, a_rows, b_rows, 0, lane);
+      fr.template read_a<0>(st0, a_rows, 0, lane);
+      fr.template read_b<0>(st0 + OPB, b_rows, 0, lane);
     }
-    // Steady state: four stages per trip with static ring slots, every stage
-    // issuing the loads of stage s + 3 (needs s + 6 < nk for the last one):
-    // its A tile during the first sub-step, its B tile during the second. At
-    // the wait, A and B of stage s + 2 and A of stage s + 3 may still be in
-    // flight.
+    zero_acc();
+    // steady state (stage s + 4 exists): static slots and parities
     auto step = [&](int s, auto J) {
       constexpr int j = decltype(J)::value;
-      issue_a(s + 3, st[(j + 3) & 3]);
-      f1.read(st[j], a_rows, b_rows, 1, lane);
-      f0.mma(acc);
-      interleave<F::kReads, L / 2>();
-      wait_vmcnt<L + L / 2>();
-      lds_barrier();
-      issue_b(s + 3, st[(j + 3) & 3]);
-      f0.read(st[(j + 1) & 3], a_rows, b_rows, 0, lane);
-      f1.mma(acc);
-      interleave<F::kReads, L / 2>();
+      char* cur = st[j];
+      char* nx = st[(j + 1) & 3];
+      fr.template step<(j & 1), PW, true>(
+          acc, cur, cur + OPB, 0, nx, nx + OPB, 0, a_rows, b_rows, lane,
+          [&] {
+            wait_vmcnt<2 * L>();
+            lds_barrier();
+          },
+          [&](int q, int k) {
+            if (q == 2) issue_a(s + 4, cur, k, k + 1);
+            else if (q == 3) issue_b(s + 4, cur, k, k + 1);
+          });
     };
     int s = 0;
-    for (; s + 7 <= nk; s += 4) {
+    for (; s + 8 <= nk; s += 4) {
       step(s, std::integral_constant<int, 0>{});
       step(s + 1, std::integral_constant<int, 1>{});
       step(s + 2, std::integral_constant<int, 2>{});
       step(s + 3, std::integral_constant<int, 3>{});
     }
-    // Last stages: same order with run-time slot selection and counts.
-    for (; s < nk; ++s) {
-      if (s + 3 < nk) issue(s + 3, slot(s + 3));
-      f1.read(slot(s), a_rows, b_rows, 1, lane);
-      f0.mma(acc);
-      if (s + 1 < nk) {
-        const int later = nk - (s + 2) < 2 ? nk - (s + 2) : 2;  // stages issued after s + 1
-        if (later >= 2) wait_vmcnt<2 * L>();
-        else if (later == 1) wait_vmcnt<L>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        f0.read(slot(s + 1), a_rows, b_rows, 0, lane);
-      }
-      f1.mma(acc);
+    // Last stages: the same order with run-time slot selection and counts,
+    // two at a time so that each step keeps a fixed parity (one copy of the
+    // MFMA sequence per parity). The last step also reads the fragments of
+    // a step that does not come; its slot holds an older stage and no load
+    // writes it any more.
+    auto tail = [&](int s, auto P) {
+      char* cur = slot(s);
+      char* nx = slot(s + 1);
+      const bool more = s + 4 < nk;
+      auto mid = [&] {
+        if (s + 1 < nk) {
+          const int last = nk - 1 < s + 3 ? nk - 1 : s + 3;  // last stage issued so far
+          if (last - (s + 1) >= 2) wait_vmcnt<2 * L>();
+          else if (last - (s + 1) == 1) wait_vmcnt<L>();
+          else wait_vmcnt<0>();
+          lds_barrier();
+        }
+      };
+      auto iss = [&](int q, int k) {
+        if (more) {
+          if (q == 2) issue_a(s + 4, cur, k, k + 1);
+          else if (q == 3) issue_b(s + 4, cur, k, k + 1);
+        }
+      };
+      fr.template step<decltype(P)::value, PW, true>(acc, cur, cur + OPB, 0, nx, nx + OPB, 0, a_rows, b_rows, lane,
+                                                      mid, iss);
+    };
+    for (; s + 2 <= nk; s += 2) {
+      tail(s, std::integral_constant<int, 0>{});
+      tail(s + 1, std::integral_constant<int, 1>{});
     }
+    if (s < nk) tail(s, std::integral_constant<int, 0>{});
   };
   constexpr bool kc = AL == KC || BL == KC;
   if (kc && A.k % BK == 0) kloop(std::false_type{});
   else kloop(std::integral_constant<bool, kc>{});
+  acc_fence<false>(acc);
   if constexpr (KIND == PLAIN) {
     if (split) {
-      // dense 256 x 256 fp32 partial tile (rows and columns past the
-      // matrix hold sums of zero operands; the reduction skips them); each
-      // lane holds 4 consecutive columns
-      float* P = g.P + (int64_t)piece * 65536;
-      const int ml = lane & 31, nl = (lane >> 5) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = a_rows[i] + ml;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = b_rows[j] + q * 8 + nl;
-            *(f32x4_t*)(P + m * 256 + n) =
-                f32x4_t{acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-          }
-      }
+      ring_partial_store(g, acc, piece, a_rows, b_rows, lane);
       return;
     }
   }
@@ -868,7 +896,8 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
 // are waited for (vmcnt counts this wave's loads in issue order), then a
 // barrier publishes stage s + 1.
 template <class E, int AL, int BL, int KIND>
-__device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], int bid, int bz) {
+__device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], int bid, int bz, int ks = 0,
+                                           int piece = -1) {
   using namespace ring;
   constexpr int BK2 = 64;
   static_assert(E::kBytes == 2, "the ring pipeline is for bf16/fp16");
@@ -885,40 +914,60 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
     else B = g.b1;
     C = g.c1;
   }
-  int a_rows[4], b_rows[4];
+  int a_rows[8], b_rows[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_rows[i] = wm * 128 + i * 32;
+  for (int i = 0; i < 8; ++i) a_rows[i] = wm * 128 + i * 16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    b_rows[j] = (KIND == GATEUP) ? (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+  for (int j = 0; j < 8; ++j)
+    b_rows[j] = (KIND == GATEUP) ? (j < 4 ? 0 : 128) + wn * 64 + (j & 3) * 16 : wn * 128 + j * 16;
 
-  f32x16_t acc[4][4];
+  // zeroed inside the K loop, after its prologue: the fence makes the zeros
+  // opaque, and live across the prologue they were spilled, not rebuilt
+  f32x4_t acc[8][8];
+  auto zero_acc = [&] {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{};
+    acc_fence<true>(acc);
+  };
 
   Dma<AL, BK2> da;
   Dma<BL, BK2> db;
   da.init(A, m0, wave, lane);
   db.init(B, n0, wave, lane, KIND == GATEUP && BL == KC);
   const int nk1 = (A.k + BK2 - 1) / BK2;
-  const int nk = (KIND == DX) ? 2 * nk1 : nk1;
+  // split K (a piece of a weight-gradient tile): stages [sb, sb + nk) of
+  // the K loop, written as fp32 partial tile `piece`
+  const bool split = KIND == PLAIN && piece >= 0;
+  const int sb = split ? ks * g.kchunk : 0;
+  const int nk = (KIND == DX) ? 2 * nk1 : (split ? (nk1 - sb < g.kchunk ? nk1 - sb : g.kchunk) : nk1);
   constexpr int NT = Geo<BK2>::PPW;  // loads per wave per operand tile
-  // K-major descriptors, built once per tile: [0] the operand (DX: its first
-  // half, (dG, Wg)), [1] DX's second half (dU, Wu)
+  // descriptors (K-major) and M/N-major sources built once per tile: [0]
+  // the operand (DX: its first half, (dG, Wg)), [1] DX's second half (dU, Wu)
   using DA = Dma<AL, BK2>;
   using DB = Dma<BL, BK2>;
   __amdgpu_buffer_rsrc_t ra[2], rb[2];
+  typename DA::McSrc ma[1];
+  typename DB::McSrc mb[2];
   if constexpr (AL == KC) {
     ra[0] = DA::kc_rsrc(KIND == DX ? g.a0 : A, m0);
     ra[1] = KIND == DX ? DA::kc_rsrc(g.a1, m0) : ra[0];
+  } else {
+    ma[0] = DA::mc_src(A, m0, A, m0 + 128, wave);
   }
   if constexpr (BL == KC) {
     // gate/up: B rows [0, 128) from Wg (waves 0-1), [128, 256) from Wu
     const Operand& b0 = (KIND == GATEUP && wave >= 2) ? g.b1 : (KIND == DX ? g.b0 : B);
     rb[0] = DB::kc_rsrc(b0, n0);
     rb[1] = KIND == DX ? DB::kc_rsrc(g.b1, n0) : rb[0];
+  } else if constexpr (KIND == GATEUP) {
+    mb[0] = DB::mc_src(g.b0, n0, g.b1, n0, wave);
+  } else if constexpr (KIND == DX) {
+    mb[0] = DB::mc_src(g.b0, n0, g.b0, n0 + 128, wave);
+    mb[1] = DB::mc_src(g.b1, n0, g.b1, n0 + 128, wave);
+  } else {
+    mb[0] = DB::mc_src(B, n0, B, n0 + 128, wave);
   }
 
   auto reg = [&](int t) -> char* {
@@ -935,29 +984,28 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
         const bool h = s >= nk1;
         da.template issue_kcr<KT>(h ? ra[1] : ra[0], h ? g.a1.k : g.a0.k, (h ? s - nk1 : s) * BK2, t, wave, lane, j0, j1);
       } else if constexpr (AL == KC) {
-        da.template issue_kcr<KT>(ra[0], A.k, s * BK2, t, wave, lane, j0, j1);
+        da.template issue_kcr<KT>(ra[0], A.k, (sb + s) * BK2, t, wave, lane, j0, j1);
       } else {
-        da.issue_mc(A, m0, A, m0 + 128, s * BK2, t, wave, j0, j1);
+        da.issue_mcs(ma[0], (sb + s) * BK2, t, wave, j0, j1);
       }
     };
-    auto issue_b = [&](int s, char* t) {
+    auto issue_b = [&](int s, char* t, int j0 = 0, int j1 = NT) {
       if constexpr (KIND == DX) {
         const bool h = s >= nk1;
-        const Operand& op = h ? g.b1 : g.b0;
-        if constexpr (BL == KC) db.template issue_kcr<KT>(h ? rb[1] : rb[0], op.k, (h ? s - nk1 : s) * BK2, t, wave, lane);
-        else db.issue_mc(op, n0, op, n0 + 128, (h ? s - nk1 : s) * BK2, t, wave);
-      } else if constexpr (KIND == GATEUP) {
-        if constexpr (BL == KC) db.template issue_kcr<KT>(rb[0], (wave >= 2 ? g.b1 : g.b0).k, s * BK2, t, wave, lane);
-        else db.issue_mc(g.b0, n0, g.b1, n0, s * BK2, t, wave);
+        if constexpr (BL == KC)
+          db.template issue_kcr<KT>(h ? rb[1] : rb[0], h ? g.b1.k : g.b0.k, (h ? s - nk1 : s) * BK2, t, wave, lane, j0,
+                                    j1);
+        else db.issue_mcs(h ? mb[1] : mb[0], (h ? s - nk1 : s) * BK2, t, wave, j0, j1);
       } else if constexpr (BL == KC) {
-        db.template issue_kcr<KT>(rb[0], B.k, s * BK2, t, wave, lane);
+        db.template issue_kcr<KT>(rb[0], KIND == GATEUP ? (wave >= 2 ? g.b1 : g.b0).k : B.k, (sb + s) * BK2, t, wave,
+                                  lane, j0, j1);
       } else {
-        db.issue_mc(B, n0, B, n0 + 128, s * BK2, t, wave);
+        db.issue_mcs(mb[0], (sb + s) * BK2, t, wave, j0, j1);
       }
     };
 
-    using F = RFrags<E, AL, BL, BK2>;
-    F f0, f1;
+    using F = RingFrags<E, AL, BL, BK2>;
+    F fr;
     if (nk > 0) {
       issue_a(0, R[0]);
       issue_b(0, R[1]);
@@ -968,12 +1016,17 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
         wait_vmcnt<0>();
       }
       lds_barrier();
-      f0.read(R[0], R[1], a_rows, b_rows, 0, lane);
+      fr.template read_a<0>(R[0], a_rows, 0, lane);
+      fr.template read_b<0>(R[1], b_rows, 0, lane);
     }
-    // One stage. `full`: stages s + 1 and s + 2 exist (known at compile time in
-    // the unrolled loop); otherwise the tail checks at run time.
-    // The loads are spread over the sub-steps: B of stage s + 1 (needed first)
-    // over the first, A of stage s + 2 over the second and third.
+    zero_acc();
+    // One stage: two 32-K steps, the first of even parity, the second odd.
+    // `full`: stages s + 1 and s + 2 exist (known at compile time in the
+    // unrolled loop); otherwise the tail checks at run time. The first step
+    // issues B of stage s + 1 (Q0, Q1) and A of stage s + 2 (Q2, Q3); its
+    // successor is the same stage at K 32..63, so it needs no barrier. The
+    // second step's barrier (between its Q1 and Q2) publishes stage s + 1,
+    // whose first fragments its Q2 and Q3 read.
     auto stage = [&](int s, char* ca, char* cb, char* na, char* nb, char* na2, bool full) {
       const bool more = full || s + 1 < nk;
       const bool more2 = full || s + 2 < nk;
@@ -981,24 +1034,22 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
       // gathered up to 14 loads of neighbouring stages into one burst
       // (dA + dSwiGLU 4 % slower); dI measured no better with it
       if constexpr (KIND != DX) __builtin_amdgcn_sched_barrier(0);
-      if (more) issue_b(s + 1, nb);
-      f1.read(ca, cb, a_rows, b_rows, 1, lane);
-      f0.mma(acc);
-      interleave<F::kReads, NT>();
-      if (more2) issue_a(s + 2, na2, 0, NT / 2);
-      f0.read(ca, cb, a_rows, b_rows, 2, lane);
-      f1.mma(acc);
-      interleave<F::kReads, NT / 2>();
-      if (more2) issue_a(s + 2, na2, NT / 2, NT);
-      f1.read(ca, cb, a_rows, b_rows, 3, lane);
-      f0.mma(acc);
-      interleave<F::kReads, NT / 2>();
-      if (more2) wait_vmcnt<NT>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (more) f0.read(na, nb, a_rows, b_rows, 0, lane);
-      f1.mma(acc);
-      interleave<F::kReads, 0>();
+      static_assert(NT == 8, "four loads per quadrant");
+      fr.template step<0, 4, true>(acc, ca, cb, 0, ca, cb, 1, a_rows, b_rows, lane, [] {}, [&](int q, int k) {
+        if (q < 2) {
+          if (more) issue_b(s + 1, nb, 4 * q + k, 4 * q + k + 1);
+        } else if (more2) {
+          issue_a(s + 2, na2, 4 * (q - 2) + k, 4 * (q - 2) + k + 1);
+        }
+      });
+      auto mid = [&] {
+        if (more2) wait_vmcnt<NT>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+      };
+      // (the last stage reads fragments of a stage that does not come, from
+      // arrays no load writes any more)
+      fr.template step<1, 4, true>(acc, ca, cb, 1, na, nb, 0, a_rows, b_rows, lane, mid, [](int, int) {});
     };
     int s = 0;
     for (; s + 7 <= nk; s += 5) {
@@ -1013,17 +1064,36 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
   constexpr bool kc = AL == KC || BL == KC;
   if (kc && A.k % BK2 == 0) kloop(std::false_type{});
   else kloop(std::integral_constant<bool, kc>{});
+  acc_fence<false>(acc);
+  if constexpr (KIND == PLAIN) {
+    if (split) {
+      ring_partial_store(g, acc, piece, a_rows, b_rows, lane);
+      return;
+    }
+  }
   // (a select, not R[wave]: indexing R at run time would keep it in scratch)
   ring_epilogue<E, KIND>(g, C, acc, m0, n0, wm, wn, lane, reg(wave));
 }
 
 // Pipeline per operand layouts: 4 = four stages of 32 K (ring_tile), 5 =
 // five-array ring of 64 K stages (ring5_tile). Measured at D = 4096,
-// H = 11008, T = 65536 (bf16): the 64 K stages help where both operands are
-// K-major and cost a few percent where one is M/N-major.
+// H = 11008, T = 65536 (bf16): with a K-major A operand the 64 K stages are
+// the faster (gate/up 4 %, down 7 %: half the stage barriers per K).
 template <int AL, int BL>
 constexpr int ring_variant() {
-  return (AL == KC && BL == KC) ? 5 : 4;
+  return AL == KC ? 5 : 4;
+}
+// The weight gradients (both operands M/N-major, split over K at the edge):
+// the five-array ring for [dWg | dWu] (stage 4), the four-stage ring for
+// dWd (stage 3), each the faster on its shapes at D = 4096, H = 11008,
+// T = 65536.
+template <int STAGE>
+constexpr int wgrad_variant() {
+  return STAGE == 3 ? 4 : 5;
+}
+template <int STAGE>
+constexpr int wgrad_bk() {
+  return wgrad_variant<STAGE>() == 5 ? 64 : ring::BK;
 }
 
 template <class E, int AL, int BL, int KIND>
@@ -1033,12 +1103,12 @@ __device__ __forceinline__ void any_ring_tile(const KArgs& g, char* const (&R)[5
 }
 
 // A K range of a tile (piece `piece` of a split weight-gradient tile, K
-// stages [ks * kchunk, ...)): only the four-stage ring runs one.
-template <class E, int AL, int BL>
+// stages [ks * kchunk, ...) of the ring's own stage depth).
+template <class E, int AL, int BL, int STAGE>
 __device__ __forceinline__ void ring_tile_piece(const KArgs& g, char* const (&R)[5], int bid, int bz, int ks,
                                                 int piece) {
-  static_assert(ring_variant<AL, BL>() == 4, "split weight-gradient tiles need ring_tile");
-  ring_tile<E, AL, BL, PLAIN>(g, R[0], R[1], R[2], R[3], bid, bz, ks, piece);
+  if constexpr (wgrad_variant<STAGE>() == 5) ring5_tile<E, AL, BL, PLAIN>(g, R, bid, bz, ks, piece);
+  else ring_tile<E, AL, BL, PLAIN>(g, R[0], R[1], R[2], R[3], bid, bz, ks, piece);
 }
 
 // Four 32 KiB LDS arrays, and a fifth when a five-array ring runs.
@@ -1071,7 +1141,7 @@ ring_gemm(const KArgs g) {
 template <class E, int AL, int BL, int STAGE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ring_wgrad(const KArgs g) {
-  SWIGLU_RING_LDS((ring_variant<AL, BL>() == 5))
+  SWIGLU_RING_LDS((wgrad_variant<STAGE>() == 5))
   const int nt = g.tiles_m * g.tiles_n;
   const int b = blockIdx.x;
   int item = b, ks = 0, piece = -1;
@@ -1080,7 +1150,7 @@ ring_wgrad(const KArgs g) {
     item = g.n_full + piece / g.ksplit;
     ks = piece % g.ksplit;
   }
-  ring_tile_piece<E, AL, BL>(g, R, item % nt, item / nt, ks, piece);
+  ring_tile_piece<E, AL, BL, STAGE>(g, R, item % nt, item / nt, ks, piece);
 }
 
 
@@ -1773,13 +1843,13 @@ static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
 
 // Tile walk of the ring kernels (tile_coords): each XCD runs group_m M-tiles
 // x (32 / group_m) N-tiles at a time, so that its concurrent tiles share
-// operand rows through its L2. Per stage, measured over 2, 4 and 8 at
-// D = 4096, H = 11008, T = 65536 (the differences are 0.5-3 %): 2 for
-// gate/up, 8 for dA + dSwiGLU, 4 for the others (down, dI and the weight
-// gradients).
+// operand rows through its L2. Per stage, measured over 1, 2, 4 and 8 at
+// D = 4096, H = 11008, T = 65536 (the differences are 0.5-5 %): 2 for
+// gate/up and down (stage 1), 8 for dA + dSwiGLU, 4 for the others (dI and
+// the weight gradients).
 template <int KIND, int STAGE>
 constexpr int ring_group_m() {
-  return KIND == DSWIGLU ? 8 : KIND == GATEUP ? 2 : 4;
+  return KIND == DSWIGLU ? 8 : KIND == GATEUP ? 2 : STAGE == 1 ? 2 : 4;
 }
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -1824,8 +1894,8 @@ static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
 struct WgradPlan {
   int n_full, n_split, ksplit, kchunk;
 };
-static WgradPlan wgrad_plan(int nt, int64_t K, int ncu) {
-  const int nk = cdiv(K, ring::BK);
+static WgradPlan wgrad_plan(int nt, int64_t K, int ncu, int bk) {
+  const int nk = cdiv(K, bk);  // K stages of the ring that runs the tiles
   WgradPlan p{nt, 0, 1, nk};
   const int rem = nt % ncu;
   if (rem == 0) return p;
@@ -1854,7 +1924,7 @@ template <class E, int AL, int BL, int STAGE>
 static int launch_ring_wgrad(KArgs a, int grid_z, float* P, hipStream_t stream) {
   const int nt = a.tiles_m * a.tiles_n;
   if (nt <= 0) return SWIGLU_OK;
-  const WgradPlan pl = wgrad_plan(nt * grid_z, a.a0.k, dev_ncu());
+  const WgradPlan pl = wgrad_plan(nt * grid_z, a.a0.k, dev_ncu(), wgrad_bk<STAGE>());
   a.planes = grid_z;
   a.group_m = ring_group_m<PLAIN, STAGE>();
   a.P = pl.n_split ? P : nullptr;
@@ -1875,8 +1945,8 @@ static int launch_ring_wgrad(KArgs a, int grid_z, float* P, hipStream_t stream) 
 // the larger of dWd ([H, D]) and [dWg | dWu] (2 x [D, H]).
 static inline size_t splitk_bytes(int64_t T, int64_t D, int64_t H) {
   const int ncu = dev_ncu();
-  const WgradPlan pd = wgrad_plan(cdiv(H, 256) * cdiv(D, 256), T, ncu);
-  const WgradPlan pg = wgrad_plan(cdiv(D, 256) * cdiv(H, 256) * 2, T, ncu);
+  const WgradPlan pd = wgrad_plan(cdiv(H, 256) * cdiv(D, 256), T, ncu, wgrad_bk<3>());
+  const WgradPlan pg = wgrad_plan(cdiv(D, 256) * cdiv(H, 256) * 2, T, ncu, wgrad_bk<4>());
   const size_t bd = (size_t)pd.n_split * pd.ksplit * 65536 * 4, bg = (size_t)pg.n_split * pg.ksplit * 65536 * 4;
   return bd > bg ? bd : bg;
 }

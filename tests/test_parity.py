@@ -95,7 +95,7 @@ def test_weight_gradient_split_remainder_ragged(mlp):
     """Weight gradients with whole rounds of tiles plus split leftovers, on
     ragged edges: at T=8192, D=1032, H=6664 (256 x 256 tiles: 5 x 27 per
     plane), [dWg | dWu] has 270 tiles, one round of 256 on the 256 CUs and
-    14 tiles split over K into 10 pieces; dWd's 135 tiles, under one round,
+    14 tiles split over K into 8 pieces; dWd's 135 tiles, under one round,
     are all split (3 pieces). Everything against the oracle in full."""
     _check_full(mlp, make_inputs(8192, 1032, 6664, seed=8192, dtype="bf16"), "bf16",
                 "split remainder T=8192 D=1032 H=6664", check_planes=False)
