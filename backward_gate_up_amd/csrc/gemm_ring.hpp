@@ -233,6 +233,30 @@ __device__ __forceinline__ u32x4_t frag(const char* tile, int ro, int ks, int la
   }
 }
 
+// Half h of an M/N-major fragment (K rows + 4h of each lane's 8): one
+// ds_read_b64_tr_b16 into registers 2h, 2h + 1 of d.
+template <int BKT>
+__device__ __forceinline__ void frag_half(u32x4_t& d, const char* tile, int ro, int ks, int lane, int h) {
+  const int krow = ks * 32 + (lane >> 4) * 8 + ((lane & 15) >> 2) + 4 * h;
+  const int col = ro + (lane & 3) * 4;
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + mc_off<BKT>(krow, col)));
+  u32x2_t v2 = __builtin_bit_cast(u32x2_t, v);
+  if (h == 0) { d[0] = v2[0]; d[1] = v2[1]; } else { d[2] = v2[0]; d[3] = v2[1]; }
+}
+// The LDS reads of a group after MFMA n of a quadrant: K-major, fragment
+// n / 2 after each even n < 8; M/N-major, half n % 2 of fragment n / 2 after
+// each n < 8 (one transposing read per MFMA).
+template <int LAYOUT, int BKT>
+__device__ __forceinline__ void read_piece(u32x4_t (&g)[4], const char* tile, const int (&rows)[8], int r0, int ks,
+                                           int lane, int n) {
+  if (n >= 8) return;
+  if constexpr (LAYOUT == KC) {
+    if (n % 2 == 0) g[n / 2] = frag<KC, BKT>(tile, rows[r0 + n / 2], ks, lane);
+  } else {
+    frag_half<BKT>(g[n / 2], tile, rows[r0 + n / 2], ks, lane, n % 2);
+  }
+}
+
 // One wave's fragments for the 32-K steps of its 128 x 128 block, in four
 // groups of four: A rows 0-63 and 64-127 (a[0], a[1]) and B columns 0-63 and
 // 64-127 (b[0], b[1]), 64 registers. A step runs four quadrants of 16 MFMAs,
@@ -249,10 +273,10 @@ __device__ __forceinline__ u32x4_t frag(const char* tile, int ro, int ks, int la
 //
 // The MFMAs are volatile statements, and the compiler keeps loads and LDS
 // reads in their source order around them, so the interleave written here
-// is the one issued: fragment k of a quadrant's group is read after its
-// MFMA 2k (spread over half the quadrant: the M/N-major weight-gradient
-// kernels, two transposing reads per fragment, measured 1.5 % faster than
-// with the reads after MFMAs 0-3), and its NL global loads follow MFMAs 1,
+// is the one issued: the reads of a quadrant's group are spread over its
+// first 8 MFMAs (read_piece; measured 1.5-2.5 % faster for the M/N-major
+// weight gradients than all reads after MFMAs 0-3), and its NL global loads
+// follow MFMAs 1,
 // 1 + 16/NL, ... (all four waves leave a barrier together; loads issued back
 // to back would queue at the texture unit at once and hold up the MFMA issue
 // behind them).
@@ -305,20 +329,20 @@ struct RingFrags {
     // Q0 and Q1 take the B group read in the quadrant before, Q2 the A
     // group; Q3 has none new
     quad<0, F, true>(acc, [&](int n) {
-      if (n % 2 == 0 && n < 8) b[S][n / 2] = frag<BL, BKT>(bt, br[4 * S + n / 2], ks, lane);
+      read_piece<BL, BKT>(b[S], bt, br, 4 * S, ks, lane, n);
       load(0, n);
     });
     quad<0, S, true>(acc, [&](int n) {
-      if (n % 2 == 0 && n < 8) a[1][n / 2] = frag<AL, BKT>(at, ar[4 + n / 2], ks, lane);
+      read_piece<AL, BKT>(a[1], at, ar, 4, ks, lane, n);
       load(1, n);
     });
     mid();
     quad<1, S, false>(acc, [&](int n) {
-      if (NX && n % 2 == 0 && n < 8) a[0][n / 2] = frag<AL, BKT>(nat, ar[n / 2], nks, lane);
+      if (NX) read_piece<AL, BKT>(a[0], nat, ar, 0, nks, lane, n);
       load(2, n);
     });
     quad<1, F, false>(acc, [&](int n) {
-      if (NX && n % 2 == 0 && n < 8) b[S][n / 2] = frag<BL, BKT>(nbt, br[4 * S + n / 2], nks, lane);
+      if (NX) read_piece<BL, BKT>(b[S], nbt, br, 4 * S, nks, lane, n);
       load(3, n);
     });
   }
