@@ -63,6 +63,9 @@ def _check_full(mlp, inp, fmt, label, check_planes=True):
 @pytest.mark.parametrize("T,D,H", [
     (1, 64, 64), (3, 64, 128), (5, 136, 200), (40, 264, 520), (64, 200, 136),
     (127, 256, 384), (129, 512, 264), (300, 1024, 2816), (513, 256, 512), (1000, 384, 648), (777, 136, 200),
+    # T > 512 with D = 104 and 40: the five-array K loops over D have 2 stages
+    # (the second with a K tail) and 1 stage
+    (600, 104, 200), (530, 40, 72),
 ])
 def test_ragged_shapes_bf16(mlp, T, D, H):
     inp = make_inputs(T, D, H, seed=T + D + H, dtype="bf16")
