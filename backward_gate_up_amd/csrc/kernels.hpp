@@ -1844,12 +1844,12 @@ static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
 // Tile walk of the ring kernels (tile_coords): each XCD runs group_m M-tiles
 // x (32 / group_m) N-tiles at a time, so that its concurrent tiles share
 // operand rows through its L2. Per stage, measured over 1, 2, 4 and 8 at
-// D = 4096, H = 11008, T = 65536 (the differences are 0.5-5 %): 2 for
-// gate/up and down (stage 1), 8 for dA + dSwiGLU, 4 for the others (dI and
-// the weight gradients).
+// D = 4096, H = 11008, T = 65536 (the differences are 0.5-6 %): 2 for
+// gate/up, down (stage 1) and dA + dSwiGLU, 4 for the others (dI and the
+// weight gradients).
 template <int KIND, int STAGE>
 constexpr int ring_group_m() {
-  return KIND == DSWIGLU ? 8 : KIND == GATEUP ? 2 : STAGE == 1 ? 2 : 4;
+  return KIND == GATEUP || KIND == DSWIGLU || STAGE == 1 ? 2 : 4;
 }
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
