@@ -1132,8 +1132,32 @@ ring_gemm(const KArgs g) {
   any_ring_tile<E, AL, BL, KIND>(g, R, blockIdx.x, blockIdx.z);
 }
 
-// Weight-gradient launch (PLAIN, K = T): items are tiles in plane-major
-// order. Items [0, n_full) run whole; each of the n_split items after them is
+// Tile and plane of weight-gradient item `item` (nt tiles per plane). Two
+// planes ([dWg | dWu], which share the A operand X) alternate within each
+// XCD's run of items: items x + 8 (2j) and x + 8 (2j + 1) are the two planes
+// of tile x + 8j, dispatched to the same XCD, so the two read each X panel
+// through one L2. Past the last full run of 8 tiles the two planes of a
+// tile are consecutive items.
+__device__ __forceinline__ void wgrad_item(int item, int nt, int planes, int& bid, int& bz) {
+  if (planes == 1) {
+    bid = item;
+    bz = 0;
+    return;
+  }
+  const int nt8 = nt & ~7;
+  if (item < 2 * nt8) {
+    const int j = item >> 3;
+    bz = j & 1;
+    bid = ((j >> 1) << 3) | (item & 7);
+  } else {
+    const int r = item - 2 * nt8;
+    bz = r & 1;
+    bid = nt8 + (r >> 1);
+  }
+}
+
+// Weight-gradient launch (PLAIN, K = T): items are (tile, plane) pairs in
+// wgrad_item's order. Items [0, n_full) run whole; each of the n_split items after them is
 // split into ksplit pieces over K (workgroup n_full + r * ksplit + s is piece
 // s of item n_full + r), which write fp32 partial tiles for
 // splitk_reduce_tiles. The split covers only the last, partly filled round of
@@ -1150,7 +1174,9 @@ ring_wgrad(const KArgs g) {
     item = g.n_full + piece / g.ksplit;
     ks = piece % g.ksplit;
   }
-  ring_tile_piece<E, AL, BL, STAGE>(g, R, item % nt, item / nt, ks, piece);
+  int bid, bz;
+  wgrad_item(item, nt, g.planes, bid, bz);
+  ring_tile_piece<E, AL, BL, STAGE>(g, R, bid, bz, ks, piece);
 }
 
 
@@ -1774,8 +1800,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_tiles(const KArgs g, const 
   if (i >= (int64_t)g.n_split * 16384) return;
   const int r = (int)(i >> 14), rr = (int)(i >> 6) & 255, cq = (int)i & 63;
   const int nt = g.tiles_m * g.tiles_n, item = g.n_full + r;
-  int tm, tn;
-  tile_coords(item % nt, g.tiles_m, g.tiles_n, g.group_m > 0 ? g.group_m : 8, tm, tn);
+  int bid, bz, tm, tn;
+  wgrad_item(item, nt, g.planes, bid, bz);
+  tile_coords(bid, g.tiles_m, g.tiles_n, g.group_m > 0 ? g.group_m : 8, tm, tn);
   const int m = tm * 256 + rr, n = tn * 256 + cq * 4;
   if (m >= g.M || n >= g.N) return;
   const float* p = P + (int64_t)r * g.ksplit * 65536 + rr * 256 + cq * 4;
@@ -1784,7 +1811,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_tiles(const KArgs g, const 
   typename E::vec4 v;
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = E::from_f32(sum[e]);
-  *(typename E::vec4*)((item >= nt ? g.c1 : g.c0) + ((int64_t)m * g.ldc + n) * E::kBytes) = v;
+  *(typename E::vec4*)((bz ? g.c1 : g.c0) + ((int64_t)m * g.ldc + n) * E::kBytes) = v;
 }
 
 // ---------------------------------------------------------------------------
