@@ -1870,14 +1870,17 @@ static int launch_pair(KArgs a1, KArgs a2, hipStream_t stream) {
 
 // Tile walk of the ring kernels (tile_coords): each XCD runs group_m M-tiles
 // x (32 / group_m) N-tiles at a time, so that its concurrent tiles share
-// operand rows through its L2. Per stage, measured over 1, 2, 4 and 8 at
-// D = 4096, H = 11008, T = 65536 (the differences are 0.5-6 %): 2 for
-// gate/up, down (stage 1) and dA + dSwiGLU, 4 for the others (dI and the
-// weight gradients).
-template <int KIND, int STAGE>
+// operand rows through its L2. Per stage and weight layout (BL: the B
+// operand's), measured over 1, 2, 4 and 8 at D = 4096, H = 11008,
+// T = 65536 (the differences are 0.5-10 %): 2 for gate/up, down (stage 1)
+// and dA + dSwiGLU; for dI 4 with K-major weights, 1 with the nn.Linear
+// layout's N-major ones; for the weight gradients 4, except the nn.Linear
+// layout's [dWg | dWu] (planes switching the A operand): 1 (wgrad_group_m).
+template <int KIND, int STAGE, int BL>
 constexpr int ring_group_m() {
-  return KIND == GATEUP || KIND == DSWIGLU || STAGE == 1 ? 2 : 4;
+  return KIND == DX ? (BL == MC ? 1 : 4) : KIND == GATEUP || KIND == DSWIGLU || STAGE == 1 ? 2 : 4;
 }
+static inline int wgrad_group_m(bool plane_a) { return plane_a ? 1 : 4; }
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
@@ -1902,7 +1905,7 @@ static inline double ring_tile_us(int64_t K) { return 2.0 * 256 * 256 * (double)
 
 template <class E, int AL, int BL, int KIND, int STAGE>
 static int launch_ring(KArgs a, int grid_z, hipStream_t stream) {
-  a.group_m = ring_group_m<KIND, STAGE>();
+  a.group_m = ring_group_m<KIND, STAGE, BL>();
   const int nb = a.tiles_m * a.tiles_n;
   a.planes = grid_z;
   if (nb <= 0) return SWIGLU_OK;
@@ -1953,7 +1956,7 @@ static int launch_ring_wgrad(KArgs a, int grid_z, float* P, hipStream_t stream) 
   if (nt <= 0) return SWIGLU_OK;
   const WgradPlan pl = wgrad_plan(nt * grid_z, a.a0.k, dev_ncu(), wgrad_bk<STAGE>());
   a.planes = grid_z;
-  a.group_m = ring_group_m<PLAIN, STAGE>();
+  a.group_m = wgrad_group_m(a.plane_a != 0);
   a.P = pl.n_split ? P : nullptr;
   a.kchunk = pl.kchunk;
   a.n_full = pl.n_full;
