@@ -153,9 +153,10 @@ struct Dma {
   }
 
   // An M/N-major operand as this wave reads it (waves 0-1: columns from c0
-  // of op0, waves 2-3: from c1 of op1), built once per tile so that a stage
-  // costs one multiply-add for its base and, only on the stage that reaches
-  // the last K row, the exact size of the descriptor.
+  // of op0, waves 2-3: from c1 of op1), built once per tile. The K loops
+  // carry the first row of the next stage to load from stage to stage (one
+  // 64-bit add of stride()); only the stage that reaches the last K row has a
+  // descriptor of its own size.
   struct McSrc {
     const char* base;  // K row 0, column cs
     int64_t rowb;      // bytes per K row
@@ -177,10 +178,22 @@ struct Dma {
   // dimension stay below 2^31 bytes (the shape limit), so the size is int32.
   __device__ __forceinline__ void issue_mcs(const McSrc& m, int k0, char* tile, int wave, int j0 = 0,
                                            int j1 = G::PPW) {
+    issue_mcp(m, m.base + (int64_t)k0 * m.rowb, k0, tile, wave, j0, j1);
+  }
+  // Bytes per stage of BKT K rows.
+  __device__ __forceinline__ static int64_t stride(const McSrc& m) { return BKT * m.rowb; }
+  // The same with the stage's first row at hand: row = base + k0 * rowb. The
+  // last stage's size depends only on the operand (loop-invariant), so a
+  // stage costs two compares and selects for it; a stage past K (k0 >= kk)
+  // gets an empty descriptor.
+  __device__ __forceinline__ void issue_mcp(const McSrc& m, const char* row, int k0, char* tile, int wave,
+                                           int j0 = 0, int j1 = G::PPW) {
     const int rb = (int)m.rowb;
-    int n = k0 + BKT < m.kk ? BKT * rb : (m.kk - k0) * rb - m.cs2;
-    n = n < 0 ? 0 : n;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc32(m.base + (int64_t)k0 * m.rowb, n);
+    const int klast = ((m.kk - 1) / BKT) * BKT;  // first K row of the last stage
+    int tail = (m.kk - klast) * rb - m.cs2;
+    tail = tail < 0 ? 0 : tail;
+    const int n = k0 + BKT < m.kk ? BKT * rb : (k0 < m.kk ? tail : 0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc32(row, n);
 #pragma unroll
     for (int j = 0; j < G::PPW; ++j) {
       if (j < j0 || j >= j1) continue;

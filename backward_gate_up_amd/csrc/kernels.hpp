@@ -799,6 +799,25 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
       issue_a(s, stg, 0, PW);
       issue_b(s, stg, 0, PW);
     };
+    // M/N-major sources: the first K row of the stage a step loads (s + 4),
+    // carried from step to step (a 64-bit add, not a multiply, per stage)
+    constexpr bool MA = AL == MC && KIND != DX, MB = BL == MC && KIND != DX;
+    const char* pa = nullptr;
+    const char* pb = nullptr;
+    if constexpr (MA) pa = ma[0].base + (int64_t)((sb + 4) * BK) * ma[0].rowb;
+    if constexpr (MB) pb = mb[0].base + (int64_t)((sb + 4) * BK) * mb[0].rowb;
+    auto issue_a4 = [&](int s, char* stg, int j0, int j1) {
+      if constexpr (MA) da.issue_mcp(ma[0], pa, (sb + s) * BK, stg, wave, j0, j1);
+      else issue_a(s, stg, j0, j1);
+    };
+    auto issue_b4 = [&](int s, char* stg, int j0, int j1) {
+      if constexpr (MB) db.issue_mcp(mb[0], pb, (sb + s) * BK, stg + OPB, wave, j0, j1);
+      else issue_b(s, stg, j0, j1);
+    };
+    auto advance = [&] {
+      if constexpr (MA) pa += DA::stride(ma[0]);
+      if constexpr (MB) pb += DB::stride(mb[0]);
+    };
     using F = RingFrags<E, AL, BL>;
     F fr;
     // Stage s is one step. Its fragments are read from Q2 of stage s - 1 to
@@ -832,9 +851,10 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
             lds_barrier();
           },
           [&](int q, int k) {
-            if (q == 2) issue_a(s + 4, cur, k, k + 1);
-            else if (q == 3) issue_b(s + 4, cur, k, k + 1);
+            if (q == 2) issue_a4(s + 4, cur, k, k + 1);
+            else if (q == 3) issue_b4(s + 4, cur, k, k + 1);
           });
+      advance();
     };
     int s = 0;
     for (; s + 8 <= nk; s += 4) {
@@ -863,12 +883,13 @@ __device__ __forceinline__ void ring_tile(const KArgs& g, char* st0, char* st1, 
       };
       auto iss = [&](int q, int k) {
         if (more) {
-          if (q == 2) issue_a(s + 4, cur, k, k + 1);
-          else if (q == 3) issue_b(s + 4, cur, k, k + 1);
+          if (q == 2) issue_a4(s + 4, cur, k, k + 1);
+          else if (q == 3) issue_b4(s + 4, cur, k, k + 1);
         }
       };
       fr.template step<decltype(P)::value, PW, true>(acc, cur, cur + OPB, 0, nx, nx + OPB, 0, a_rows, b_rows, lane,
                                                       mid, iss);
+      advance();
     };
     for (; s + 2 <= nk; s += 2) {
       tail(s, std::integral_constant<int, 0>{});
@@ -1007,6 +1028,23 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
       }
     };
 
+    // M/N-major sources: the first K row of the stage each operand loads
+    // next (B: s + 1, A: s + 2), carried from stage to stage (a 64-bit add,
+    // not a multiply, per stage)
+    constexpr bool MA = AL == MC && KIND != DX, MB = BL == MC && KIND != DX;
+    const char* pa = nullptr;
+    const char* pb = nullptr;
+    if constexpr (MA) pa = ma[0].base + (int64_t)((sb + 2) * BK2) * ma[0].rowb;
+    if constexpr (MB) pb = mb[0].base + (int64_t)((sb + 1) * BK2) * mb[0].rowb;
+    auto issue_a2 = [&](int s, char* t, int j0, int j1) {
+      if constexpr (MA) da.issue_mcp(ma[0], pa, (sb + s) * BK2, t, wave, j0, j1);
+      else issue_a(s, t, j0, j1);
+    };
+    auto issue_b1 = [&](int s, char* t, int j0, int j1) {
+      if constexpr (MB) db.issue_mcp(mb[0], pb, (sb + s) * BK2, t, wave, j0, j1);
+      else issue_b(s, t, j0, j1);
+    };
+
     using F = RingFrags<E, AL, BL, BK2>;
     F fr;
     if (nk > 0) {
@@ -1040,9 +1078,9 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
       static_assert(NT == 8, "four loads per quadrant");
       fr.template step<0, 4, true>(acc, ca, cb, 0, ca, cb, 1, a_rows, b_rows, lane, [] {}, [&](int q, int k) {
         if (q < 2) {
-          if (more) issue_b(s + 1, nb, 4 * q + k, 4 * q + k + 1);
+          if (more) issue_b1(s + 1, nb, 4 * q + k, 4 * q + k + 1);
         } else if (more2) {
-          issue_a(s + 2, na2, 4 * (q - 2) + k, 4 * (q - 2) + k + 1);
+          issue_a2(s + 2, na2, 4 * (q - 2) + k, 4 * (q - 2) + k + 1);
         }
       });
       auto mid = [&] {
@@ -1053,6 +1091,8 @@ __device__ __forceinline__ void ring5_tile(const KArgs& g, char* const (&R)[5], 
       // (the last stage reads fragments of a stage that does not come, from
       // arrays no load writes any more)
       fr.template step<1, 4, true>(acc, ca, cb, 1, na, nb, 0, a_rows, b_rows, lane, mid, [](int, int) {});
+      if constexpr (MA) pa += DA::stride(ma[0]);
+      if constexpr (MB) pb += DB::stride(mb[0]);
     };
     int s = 0;
     for (; s + 7 <= nk; s += 5) {
