@@ -577,75 +577,77 @@ __device__ __forceinline__ void ring_epilogue(const KArgs& g, char* C, f32x4_t (
       pu.template store<128>(g.c2, g.ldc, r0, c0, g.M, g.N, lane);
     }
   } else if constexpr (KIND == DSWIGLU) {
-    // wave block: 128 rows x 128 hidden units, in four quarters of 32 rows
-    // (two MFMA row blocks each). The G and U rows of a quarter are loaded
-    // into LDS, turned into dG and dU in place (this tile's own (t, h) block
-    // only) and stored back. Two LDS slots of 16 KiB: the loads of quarter
-    // q + 1 are in flight while quarter q is computed and stored, and those
-    // of q + 2 go into q's slot as soon as q's results have been read back
-    // into registers, before q's stores. A quarter is 16 loads (8 per plane)
-    // and 16 stores (8 per plane, out-of-range chunks dropped by the
-    // descriptor rather than skipped), and vmcnt counts this wave's loads and
-    // stores in issue order: L0 L1 | L2 S0 | L3 S1 | S2 | S3. So waiting for
-    // the loads of quarter q never waits for a store: 16, 32, 48 and 32
-    // operations issued after them may stay outstanding.
+    // wave block: 128 rows x 128 hidden units, in eight parts of 16 rows
+    // (one MFMA row block each). The G and U rows of a part are loaded into
+    // LDS, turned into dG and dU in place (this tile's own (t, h) block only)
+    // and stored back. Four LDS slots of 8 KiB: while part q is computed and
+    // stored the loads of parts q + 1 .. q + 3 are in flight, and those of
+    // q + 4 go into q's slot as soon as q's results have been read back into
+    // registers, before q's stores (the loads wait on memory latency, so
+    // more of them in flight). A part is 8 loads (4 per plane) and 8 stores
+    // (4 per plane, out-of-range chunks dropped by the descriptor rather than
+    // skipped), and vmcnt counts this wave's loads and stores in issue order:
+    // L0 L1 L2 L3 | L4 S0 | L5 S1 | L6 S2 | L7 S3 | S4 | S5 | S6 | S7. So
+    // waiting for the loads of part q never waits for a store: 24, 32, 40,
+    // 48, 56, 48, 40 and 32 operations issued after them may stay
+    // outstanding.
     const int64_t plane_bytes = (int64_t)g.M * g.ldc * 2;
     const int c0 = n0 + wn * 128;
     auto issue = [&](int q) {
-      char* slot = wbuf + (q & 1) * 16384;
-      const int r0 = m0 + wm * 128 + q * 32;
-      WaveBlock<E, 128>{slot}.load(g.c0, g.ldc, plane_bytes, r0, c0, 32, lane);
-      WaveBlock<E, 128>{slot + 8192}.load(g.c1, g.ldc, plane_bytes, r0, c0, 32, lane);
+      char* slot = wbuf + (q & 3) * 8192;
+      const int r0 = m0 + wm * 128 + q * 16;
+      WaveBlock<E, 128>{slot}.load(g.c0, g.ldc, plane_bytes, r0, c0, 16, lane);
+      WaveBlock<E, 128>{slot + 4096}.load(g.c1, g.ldc, plane_bytes, r0, c0, 16, lane);
     };
     issue(0);
     issue(1);
+    issue(2);
+    issue(3);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q == 0) ring::wait_vmcnt<16>();
-      else if (q == 2) ring::wait_vmcnt<48>();
-      else ring::wait_vmcnt<32>();
-      WaveBlock<E, 128> pg{wbuf + (q & 1) * 16384}, pu{wbuf + (q & 1) * 16384 + 8192};
-      // every G and U value of the quarter first (one LDS latency), then
-      // the math
-      V4 gv[2][8], uv[2][8];
+    for (int q = 0; q < 8; ++q) {
+      if (q == 0) ring::wait_vmcnt<24>();
+      else if (q == 1 || q == 7) ring::wait_vmcnt<32>();
+      else if (q == 2 || q == 6) ring::wait_vmcnt<40>();
+      else if (q == 3 || q == 5) ring::wait_vmcnt<48>();
+      else ring::wait_vmcnt<56>();
+      WaveBlock<E, 128> pg{wbuf + (q & 3) * 8192}, pu{wbuf + (q & 3) * 8192 + 4096};
+      // every G and U value of the part first (one LDS latency), then the
+      // math
+      V4 gv[8], uv[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int j = 0; j < 8; ++j) {
+        gv[j] = pg.get4(ml, j * 16 + nl);
+        uv[j] = pu.get4(ml, j * 16 + nl);
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          gv[h][j] = pg.get4(h * 16 + ml, j * 16 + nl);
-          uv[h][j] = pu.get4(h * 16 + ml, j * 16 + nl);
+      for (int j = 0; j < 8; ++j) {
+        const int c = j * 16 + nl;
+        V4 dg, du;
+        float da[4], gf[4], uf[4], dgf[4], duf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          da[e] = acc[q][j][e];
+          gf[e] = E::to_f32(gv[j][e]);
+          uf[e] = E::to_f32(uv[j][e]);
         }
+        dswiglu4<E>(da, gf, uf, dgf, duf);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = h * 16 + ml, c = j * 16 + nl;
-          V4 dg, du;
-          float da[4], gf[4], uf[4], dgf[4], duf[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            da[e] = acc[2 * q + h][j][e];
-            gf[e] = E::to_f32(gv[h][j][e]);
-            uf[e] = E::to_f32(uv[h][j][e]);
-          }
-          dswiglu4<E>(da, gf, uf, dgf, duf);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dg[e] = E::from_f32(dgf[e]);
-            du[e] = E::from_f32(duf[e]);
-          }
-          pg.put4(r, c, dg);
-          pu.put4(r, c, du);
+        for (int e = 0; e < 4; ++e) {
+          dg[e] = E::from_f32(dgf[e]);
+          du[e] = E::from_f32(duf[e]);
         }
-      u32x4_t vg[8], vu[8];
-      pg.template read_chunks<8>(vg, 0, lane);
-      pu.template read_chunks<8>(vu, 0, lane);
-      // the slot's contents are in registers: quarter q + 2 may load into it
+        pg.put4(ml, c, dg);
+        pu.put4(ml, c, du);
+      }
+      u32x4_t vg[4], vu[4];
+      pg.template read_chunks<4>(vg, 0, lane);
+      pu.template read_chunks<4>(vu, 0, lane);
+      // the slot's contents are in registers: part q + 4 may load into it
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (q + 2 < 4) issue(q + 2);
-      const int r0 = m0 + wm * 128 + q * 32;
-      pg.template write_chunks<8>(vg, 0, g.c0, g.ldc, r0, c0, g.M, g.N, lane);
-      pu.template write_chunks<8>(vu, 0, g.c1, g.ldc, r0, c0, g.M, g.N, lane);
+      if (q + 4 < 8) issue(q + 4);
+      const int r0 = m0 + wm * 128 + q * 16;
+      pg.template write_chunks<4>(vg, 0, g.c0, g.ldc, r0, c0, g.M, g.N, lane);
+      pu.template write_chunks<4>(vu, 0, g.c1, g.ldc, r0, c0, g.M, g.N, lane);
     }
   } else {
     // PLAIN / DX: 128 x 128 block of C
