@@ -2245,7 +2245,16 @@ struct Path {
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(D, 256);
     if constexpr (E::kBytes == 2) return launch_ring<E, KC, FW, PLAIN, STAGE>(a, 1, s);
-    else return launch<E, 256, 256, KC, FW, PLAIN, STAGE>(a, 1, s);
+    else {
+      // fp32: with fewer 256 x 256 tiles than CUs (D / 256 per row block),
+      // 64-row tiles fill the chip (D = 2048, T = 4096: 128 tiles leave half
+      // the CUs idle; 512 64-row tiles made the step 6.5 % faster)
+      if (a.tiles_m * a.tiles_n < 256) {
+        a.tiles_m = cdiv(T, 64);
+        return launch<E, 64, 256, KC, FW, PLAIN, STAGE>(a, 1, s);
+      }
+      return launch<E, 256, 256, KC, FW, PLAIN, STAGE>(a, 1, s);
+    }
   }
 
   // Backward stage arguments (tiles_m/tiles_n filled by the launchers).
