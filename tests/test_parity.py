@@ -120,6 +120,14 @@ def test_fp32_and_fp16_ragged(mlp):
         _check_full(mlp, inp, fmt, f"{fmt} T=333 D=136 H=264")
 
 
+def test_fp32_ragged_large_t(mlp):
+    # fp32 above 512 tokens: the down projection has fewer 256 x 256 tiles
+    # than CUs and runs on 64-row tiles, here with ragged M (777 = 12 * 64 +
+    # 9) and N (136 < 256)
+    inp = make_inputs(777, 136, 200, seed=78, dtype="fp32")
+    _check_full(mlp, inp, "fp32", "fp32 T=777 D=136 H=200")
+
+
 def test_fp16_ragged_ring(mlp):
     # T > 512 takes the ring kernels; D and H leave a K tail in every stage
     # (136, 200 = 8 mod 32 and mod 64)
