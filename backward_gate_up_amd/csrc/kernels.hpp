@@ -2244,7 +2244,17 @@ struct Path {
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(D, 256);
-    if constexpr (E::kBytes == 2) return launch_ring<E, KC, FW, PLAIN, STAGE>(a, 1, s);
+    if constexpr (E::kBytes == 2) {
+      // few 256-column tiles (small D): when the 64-row tiles of the same
+      // rows still fit one round on the CUs, they beat one round of ring
+      // tiles on a quarter of them (T = 4096, D = 1024: 50 against 63 us;
+      // at two rounds of 64-row tiles the ring wins)
+      if (cdiv(T, 64) * a.tiles_n <= 256) {
+        a.tiles_m = cdiv(T, 64);
+        return launch<E, 64, 256, KC, FW, PLAIN, STAGE>(a, 1, s);
+      }
+      return launch_ring<E, KC, FW, PLAIN, STAGE>(a, 1, s);
+    }
     else {
       // fp32: with fewer 256 x 256 tiles than CUs (D / 256 per row block),
       // 64-row tiles fill the chip (D = 2048, T = 4096: 128 tiles leave half
@@ -2384,6 +2394,12 @@ struct Path {
       if ((rc = launch_ring<E, KC, BW, DSWIGLU, 2>(dgu, 1, s))) return rc;
       if ((rc = launch_ring_wgrad<E, MC, MC, 3>(dwd, 1, P, s))) return rc;
       if ((rc = launch_ring_wgrad<E, MC, MC, 4>(dwgu, 2, P, s))) return rc;
+      // dI as the down projection above (T = 4096, D = 1024: 86 against
+      // 100 us)
+      if (cdiv(T, 64) * dx.tiles_n <= 256) {
+        dx.tiles_m = cdiv(T, 64);
+        return launch<E, 64, 256, KC, BW, DX, 5>(dx, 1, s);
+      }
       return launch_ring<E, KC, BW, DX, 5>(dx, 1, s);
     } else {
       int rc = launch_pair<E, MC, MC, PLAIN, KC, BW, DSWIGLU, 8>(dwd, dgu, s);
