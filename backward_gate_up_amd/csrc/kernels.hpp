@@ -2207,7 +2207,15 @@ struct Path {
     }
     a.tiles_m = cdiv(T, 256);
     a.tiles_n = cdiv(H, 128);
-    if constexpr (E::kBytes == 2) return launch_ring<E, KC, FW, GATEUP, STAGE>(a, 1, s);
+    if constexpr (E::kBytes == 2) {
+      // few ring tiles: 64-row tiles when those fit one round (as the down
+      // projection)
+      if (cdiv(T, 64) * a.tiles_n <= 256) {
+        a.tiles_m = cdiv(T, 64);
+        return launch<E, 64, 256, KC, FW, GATEUP, STAGE>(a, 1, s);
+      }
+      return launch_ring<E, KC, FW, GATEUP, STAGE>(a, 1, s);
+    }
     else return launch<E, 256, 256, KC, FW, GATEUP, STAGE>(a, 1, s);
   }
 
@@ -2391,7 +2399,16 @@ struct Path {
       // one ring launch per step: measured 0.5 % faster than pairing the
       // short-K stages with the long-K weight gradients on the ring engine
       int rc;
-      if ((rc = launch_ring<E, KC, BW, DSWIGLU, 2>(dgu, 1, s))) return rc;
+      // dA + dSwiGLU on 64-row tiles when those fit one round (as the down
+      // projection; T = 1024, D = 1024, H = 2816: 29 against 43 us)
+      if (cdiv(T, 64) * dgu.tiles_n <= 256) {
+        KArgs d64 = dgu;
+        d64.tiles_m = cdiv(T, 64);
+        rc = launch<E, 64, 256, KC, BW, DSWIGLU, 2>(d64, 1, s);
+      } else {
+        rc = launch_ring<E, KC, BW, DSWIGLU, 2>(dgu, 1, s);
+      }
+      if (rc) return rc;
       if ((rc = launch_ring_wgrad<E, MC, MC, 3>(dwd, 1, P, s))) return rc;
       if ((rc = launch_ring_wgrad<E, MC, MC, 4>(dwgu, 2, P, s))) return rc;
       // dI as the down projection above (T = 4096, D = 1024: 86 against
